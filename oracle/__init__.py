@@ -1,0 +1,26 @@
+"""CPU oracle for the fused softmax attention forward pass (fp64).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The product path (the HIP
+library and its Python binding) never imports, calls or links it, and the two share no
+code. Modules:
+
+  attention  the plain definition in numpy float64 (full tensors, selected rows, P matrix)
+  brute      pure-Python loops with math.fsum, for tiny shapes
+  online     the pages' tiled online-softmax recurrence in float64 (to pin the identity)
+
+Every function here is pinned by ``tests/test_oracle.py`` against closed forms,
+invariants, a hand-derived worked example and brute force.
+"""
+from .attention import attention_fwd, attention_head, attention_probs, attention_rows
+from .brute import attention_brute
+from .online import attention_online
+
+__all__ = [
+    "attention_fwd",
+    "attention_head",
+    "attention_probs",
+    "attention_rows",
+    "attention_brute",
+    "attention_online",
+]

@@ -1,0 +1,130 @@
+"""Python binding of the C-ABI attention forward library (``libattn_fwd.so``).
+
+Argument marshalling only: shapes, dtypes and devices are checked, output tensors are
+allocated with torch when the caller gives none, and the C entry point is called with raw
+device pointers and the current HIP stream. Every step of the computation runs in the
+library's HIP kernels; if the library is missing this module raises instead of computing
+anything itself.
+
+C entry points (declared in include/attn_fwd.h):
+  int attn_fwd(q, k, v, o, lse, B, H, N, D, causal, scale, stream)
+  const char* attn_fwd_strerror(int code)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libattn_fwd.so"
+
+# Return codes of the C ABI (mirrors include/attn_fwd.h).
+ATTN_FWD_OK = 0
+ATTN_FWD_EINVAL = -1
+ATTN_FWD_EUNSUPPORTED = -2
+ATTN_FWD_EALIGN = -3
+ATTN_FWD_ELAUNCH = -4
+
+_lock = threading.Lock()
+_lib = None
+
+
+class AttnFwdError(RuntimeError):
+    """A nonzero return code from the C entry point."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"attn_fwd failed with code {code}: {message}")
+        self.code = code
+
+
+def library_path() -> str:
+    return os.environ.get("ATTN_FWD_LIB", os.path.join(_HERE, _LIB_NAME))
+
+
+def load_library():
+    """Load ``libattn_fwd.so`` once and declare the C signatures. Raises if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build the HIP library first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        ci = ctypes.c_int
+        lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, vp]
+        lib.attn_fwd.restype = ci
+        lib.attn_fwd_strerror.argtypes = [ci]
+        lib.attn_fwd_strerror.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def strerror(code: int) -> str:
+    return load_library().attn_fwd_strerror(int(code)).decode()
+
+
+def _current_stream_handle(device) -> int:
+    import torch
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+             stream=None):
+    """Fused softmax attention forward on the GPU.
+
+    q, k, v: contiguous bfloat16 CUDA tensors of shape [B, H, N, D], D in {64, 128}.
+    Returns (O bfloat16 [B, H, N, D], lse float32 [B, H, N]); ``out``/``lse`` may be
+    given to write in place. ``scale`` defaults to 1/sqrt(D). The call is asynchronous
+    on ``stream`` (a torch.cuda.Stream or raw handle; default: torch's current stream).
+    """
+    import torch
+
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must have shape [B, H, N, D]")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+    B, H, N, D = (int(x) for x in q.shape)
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()
+          or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, H, N] on q's device")
+    if stream is None:
+        handle = _current_stream_handle(q.device)
+    elif isinstance(stream, int):
+        handle = stream
+    else:
+        handle = int(stream.cuda_stream)
+    lib = load_library()
+    code = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, N, D, int(bool(causal)), float(scale), handle)
+    if code != ATTN_FWD_OK:
+        msg = lib.attn_fwd_strerror(code).decode()
+        if code in (ATTN_FWD_EINVAL, ATTN_FWD_EUNSUPPORTED, ATTN_FWD_EALIGN):
+            raise ValueError(f"attn_fwd rejected its arguments (code {code}): {msg}")
+        raise AttnFwdError(code, msg)
+    return out, lse

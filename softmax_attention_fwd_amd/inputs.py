@@ -1,0 +1,83 @@
+"""Seeded synthetic inputs and the five attention workloads.
+
+This module draws random numbers and nothing else: it holds none of the attention
+arithmetic, so both the HIP path's tests and the CPU oracle can take their inputs from
+it without sharing any of the method.
+
+Recipe (the pages fix none; the same recipe serves tests and the benchmark):
+  one CPU ``torch.Generator`` per call, seeded with ``seed``; draw Q, then K, then V as
+  float32 standard normals of shape [B, H, N, D]; multiply each by its sigma; round to
+  bfloat16 with round-to-nearest-even (torch's float32 -> bfloat16 cast).
+The workloads use seed 1000 + workload number.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One attention forward problem: shapes, mask, input scales."""
+    name: str
+    B: int
+    H: int
+    N: int
+    D: int
+    causal: bool
+    sigma_q: float = 1.0
+    sigma_k: float = 1.0
+    sigma_v: float = 1.0
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def flops(self) -> float:
+        """4*B*H*N^2*D, halved when causal (the throughput convention of the metric)."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.D
+        return f / 2 if self.causal else f
+
+    @property
+    def hbm_bytes(self) -> int:
+        """Algorithmic HBM bytes: Q, K, V read once and O written once (bf16), lse (fp32)."""
+        return 4 * self.B * self.H * self.N * self.D * 2 + self.B * self.H * self.N * 4
+
+    def describe(self) -> str:
+        c = "causal" if self.causal else "non-causal"
+        return f"B{self.B} H{self.H} N{self.N} D{self.D} {c}"
+
+
+# The five workloads: small parity case, two non-causal, two causal (the last with
+# Q, K ~ N(0, 2^2) so the softmax is peaky and the rescaling is exercised hard).
+WORKLOADS = {
+    1: Workload("w1_b1h1n128d64", 1, 1, 128, 64, False, seed=1001),
+    2: Workload("w2_b16h16n1024d64", 16, 16, 1024, 64, False, seed=1002),
+    3: Workload("w3_b16h16n4096d128", 16, 16, 4096, 128, False, seed=1003),
+    4: Workload("w4_b8h32n8192d128_causal", 8, 32, 8192, 128, True, seed=1004),
+    5: Workload("w5_b1h32n16384d128_causal_sigma2", 1, 32, 16384, 128, True,
+                sigma_q=2.0, sigma_k=2.0, seed=1005),
+}
+
+
+def make_qkv(B: int, H: int, N: int, D: int, seed: int, sigma_q: float = 1.0,
+             sigma_k: float = 1.0, sigma_v: float = 1.0):
+    """Q, K, V as contiguous CPU bfloat16 tensors of shape [B, H, N, D]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    out = []
+    for sigma in (sigma_q, sigma_k, sigma_v):
+        x = torch.randn((B, H, N, D), generator=g, dtype=torch.float32)
+        if sigma != 1.0:
+            x.mul_(sigma)
+        out.append(x.to(torch.bfloat16).contiguous())
+    return tuple(out)
+
+
+def workload_inputs(w: Workload):
+    """Q, K, V (CPU bfloat16) of a workload, from its own seed."""
+    return make_qkv(w.B, w.H, w.N, w.D, w.seed, w.sigma_q, w.sigma_k, w.sigma_v)
