@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Attention forward throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 3] [--gpus 1]
+
+One step = one attn_fwd call (the whole fused forward: K/V streaming, both contractions,
+online softmax, epilogue) over the workload's full tensors, already resident in HBM.
+The default workload is B16 H16 N4096 D128 non-causal with bf16 inputs. Prints ONE JSON
+line on stdout; details go to stderr.
+
+Reported:
+  value          whole-job TFLOP/s = 4*B*H*N^2*D (halved when causal) * K / (timed span)
+  roofline       the kernel's mean launch duration (HIP events on the launch stream)
+                 against the bf16 dense MFMA peak
+  cpu_baseline   the fp64 numpy oracle, timed on this host's cores on a bounded sample
+                 of the same workload (a few heads), in the same unit
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X bf16 dense MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """Time the fp64 oracle on whole heads of the workload, one head per host core."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    per_head = w.flops / (w.B * w.H)
+    heads = min(w.B * w.H, cores)
+    b_idx = [i // w.H for i in range(heads)]
+    h_idx = [i % w.H for i in range(heads)]
+    qs = np.stack([q[b, h].double().numpy() for b, h in zip(b_idx, h_idx)])[None]
+    ks = np.stack([k[b, h].double().numpy() for b, h in zip(b_idx, h_idx)])[None]
+    vs = np.stack([v[b, h].double().numpy() for b, h in zip(b_idx, h_idx)])[None]
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        if ctx:
+            ctx.__enter__()
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.attention_fwd(qs, ks, vs, w.causal, w.scale, workers=cores)
+            done += heads
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return {
+        "value": round(done * per_head / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{done} head-passes of {w.describe()} (first {heads} heads, "
+                   f"{done * per_head:.3e} flop, fp64 numpy, one head per thread) in {dt:.1f} s"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, help="1..5 (default 3)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the attention forward runs on a single MI355X "
+              "and this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from softmax_attention_fwd_amd import attn_fwd
+    from softmax_attention_fwd_amd.inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {args.workload}: {w.describe()}; generating inputs (seed {w.seed})")
+    q, k, v = workload_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        attn_fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    span0 = torch.cuda.Event(enable_timing=True)
+    span1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    span0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    span1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    total_ms = span0.elapsed_time(span1)
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    mean_launch = statistics.fmean(launch_ms)
+    ms_per_step = total_ms / args.steps
+    value = w.flops * args.steps / (total_ms * 1e-3) / 1e12
+    achieved = w.flops / (mean_launch * 1e-3) / 1e12
+    log(f"[bench] span {total_ms:.3f} ms for {args.steps} steps ({ms_per_step:.4f} ms/step, "
+        f"wall {wall * 1e3:.1f} ms); launch median {statistics.median(launch_ms):.4f} "
+        f"min {min(launch_ms):.4f} max {max(launch_ms):.4f} ms")
+    log(f"[bench] {value:.1f} TFLOP/s whole-job; kernel {achieved:.1f} TFLOP/s = "
+        f"{100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 dense peak")
+
+    result = {
+        "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak (B16 H16 N4096 D128)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q, K, V)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+                   "causal": w.causal, "scale": w.scale, "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "launch_ms": {"mean": round(mean_launch, 5), "median": round(statistics.median(launch_ms), 5),
+                      "min": round(min(launch_ms), 5), "max": round(max(launch_ms), 5)},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the fp64 oracle on host cores (~{args.cpu_seconds:.0f} s budget)")
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        log(f"[bench] cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

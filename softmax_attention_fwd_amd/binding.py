@@ -94,10 +94,10 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
             raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
         if t.dim() != 4:
             raise ValueError(f"{name} must have shape [B, H, N, D]")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
     if not (q.shape == k.shape == v.shape):
         raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
     if not (q.device == k.device == v.device):

@@ -1,0 +1,112 @@
+"""C-ABI library checks that need no GPU: it loads, exports every declared entry point,
+and rejects invalid arguments with the documented codes before any HIP call.
+
+Every call below has at least one invalid argument, so none of them reaches a launch.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from softmax_attention_fwd_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.library_path()):
+        from softmax_attention_fwd_amd import build
+        build.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(attn_fwd\w*)\s*\(", text, flags=re.M)))
+
+
+def declared_codes():
+    text = open(HEADER).read()
+    return {name: int(val) for name, val in re.findall(r"#define\s+(ATTN_FWD_\w+)\s+(-?\d+)", text)}
+
+
+def test_header_declares_entry_points():
+    assert declared_functions() == ["attn_fwd", "attn_fwd_strerror"]
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in attn_fwd.h but not exported"
+
+
+def test_codes_match_binding():
+    codes = declared_codes()
+    assert codes == {
+        "ATTN_FWD_OK": binding.ATTN_FWD_OK,
+        "ATTN_FWD_EINVAL": binding.ATTN_FWD_EINVAL,
+        "ATTN_FWD_EUNSUPPORTED": binding.ATTN_FWD_EUNSUPPORTED,
+        "ATTN_FWD_EALIGN": binding.ATTN_FWD_EALIGN,
+        "ATTN_FWD_ELAUNCH": binding.ATTN_FWD_ELAUNCH,
+    }
+
+
+def test_strerror(lib):
+    seen = set()
+    for code in declared_codes().values():
+        msg = lib.attn_fwd_strerror(code).decode()
+        assert msg and msg != "unknown error code"
+        seen.add(msg)
+    assert len(seen) == len(declared_codes())
+    assert lib.attn_fwd_strerror(12345).decode() == "unknown error code"
+
+
+# Fake, never-dereferenced addresses: validation returns before touching them.
+A = 0x10000  # 16-byte aligned
+
+
+def call(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=128, D=64, causal=0, scale=0.125):
+    return lib.attn_fwd(q, k, v, o, lse, B, H, N, D, causal, ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(lse=None), -1),
+    (dict(B=0), -1), (dict(H=0), -1), (dict(N=0), -1), (dict(N=-5), -1),
+    (dict(causal=2), -1), (dict(causal=-1), -1),
+    (dict(scale=0.0), -1), (dict(scale=-1.0), -1), (dict(scale=math.inf), -1),
+    (dict(scale=math.nan), -1),
+    (dict(D=96), -2), (dict(D=32), -2), (dict(D=256), -2), (dict(D=0), -2),
+    (dict(N=1 << 24, D=128), -1),                   # N*D reaches 2^31
+    (dict(B=1 << 16, H=1 << 16, N=1 << 10), -1),    # grid reaches 2^31 workgroups
+    (dict(q=A + 8), -3), (dict(k=A + 2), -3), (dict(v=A + 4), -3), (dict(o=A + 1), -3),
+    (dict(lse=A + 2), -3),
+])
+def test_invalid_arguments_rejected(lib, kw, code):
+    assert call(lib, **kw) == code
+
+
+def test_binding_rejects_cpu_and_bad_dtypes():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        binding.attn_fwd(q, q, q)
+    with pytest.raises(ValueError, match="bfloat16"):
+        binding.attn_fwd(q.float(), q, q)
+    with pytest.raises(ValueError, match="shape"):
+        binding.attn_fwd(q[0], q, q)
+    with pytest.raises(ValueError, match="contiguous"):
+        binding.attn_fwd(q.transpose(2, 3), q, q)
+
+
+def test_binding_missing_library_is_loud(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setenv("ATTN_FWD_LIB", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.load_library()
