@@ -31,6 +31,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "attn_fwd.h"
 
@@ -40,15 +41,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQW = 32;              // query rows per wave
 constexpr int kBr = kWaves * kQW;    // query rows per workgroup
-constexpr int kBc = 64;              // keys per K/V tile
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold, in log2 units of probability
 
 struct Params {
   const __bf16* q;
@@ -74,25 +77,103 @@ __device__ inline float sum_across_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Byte offset of 16-byte chunk `chunk` of tile row `row` (rows are D bf16 wide).
-template <int D>
-__device__ inline int lds_offset(int row, int chunk) {
-  return row * (D * 2) + ((chunk ^ (row & 7)) << 4);
+// LDS tile layout. A K or V tile is BC rows (keys) of D bf16, row-major, unpadded; its
+// 16-byte chunks are permuted within each row: logical chunk c of row r is stored at
+// physical chunk c ^ f(r & 7), with f(r) = ((r & 3) << 1) | ((r >> 2) & 1) (a 3-bit
+// rotation). f is a bijection on any 8 aligned rows, so the score MFMA's K reads (eight
+// lanes reading one chunk of eight consecutive rows) hit eight different bank groups, and
+// on any 4 aligned rows f >> 1 is distinct, so each 16-lane group of the transposing V read
+// (two adjacent chunks of four consecutive rows) also covers eight different bank groups.
+// Splitting the XOR into bit fields, every read address is one of a few per-lane bases
+// plus a compile-time offset (see k_base / v_base in the kernel).
+__device__ inline int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int D, int BC>
+struct TileLayout {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;                    // 16-byte chunks per row
+  static constexpr int kTileBytes = BC * kRowBytes;        // one K or V tile
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;    // rows one wave-wide copy fills
+  static constexpr int kCopies = kTileBytes / 1024 / kWaves;  // copies per wave per tile
+  static constexpr int kLdsBytes = 4 * kTileBytes;         // K[2], V[2]
+  static_assert(kCopies * 1024 * kWaves == kTileBytes, "tile must split into 1 KiB copies per wave");
+  static_assert(kChunks >= 8, "the chunk permutation needs 8 chunks per row");
+};
+
+// Instruction order for the steady-state block "scores of tile t+1 || exponentials of
+// tile t, then O += P V of tile t": each score MFMA is paired with its LDS operand read
+// and a share of the exponential work, then each P V MFMA with its two transposing reads.
+// This keeps the matrix cores busy while the VALU works and bounds the operand registers
+// in flight.
+template <int D, int BC>
+__device__ inline void interleave_schedule() {
+  constexpr int kQkMfma = (BC / 32) * (D / 16);
+  constexpr int kPvMfma = (BC / 16) * (D / 32);
+  constexpr int kValu = 56 * (BC / 32);  // exponential work of the tile, roughly
+#pragma unroll
+  for (int i = 0; i < kQkMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu / kQkMfma, 0);  // VALU
+  }
+#pragma unroll
+  for (int i = 0; i < kPvMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (transposing)
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+  }
 }
 
-template <int D, bool CAUSAL>
+// Buffer resource over one head's [N, D] bf16 tensor: 64-bit base, no stride, range
+// num_bytes.
+__device__ inline i32x4 make_rsrc(const void* base, uint32_t num_bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)num_bytes);
+  r[3] = 0x00020000;  // raw 32-bit buffer data format
+  return r;
+}
+
+// One 16-byte-per-lane copy global -> LDS (buffer_load_dwordx4 ... lds): lane l reads
+// rsrc.base + soff + voff[l] and writes LDS address lds + 16*l. The copy is asynchronous
+// (counted by vmcnt); wait_copies_and_barrier() completes it. It is issued from inline
+// assembly so that the compiler does not serialise unrelated LDS reads behind it; M0 is
+// used by nothing else in these kernels.
+__device__ inline void copy16_to_lds(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+      : "memory", "m0");
+}
+
+__device__ inline void wait_copies_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+__device__ inline uint32_t lds_address(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+template <int D, int BC, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const Params p) {
   static_assert(D == 64 || D == 128, "head dimension");
-  constexpr int kChunks = D / 8;                  // 16-byte chunks per row
-  constexpr int kTileBytes = kBc * D * 2;         // one K or V tile
-  constexpr int kLoads = kTileBytes / 16 / kThreads;
-  static_assert(kLoads * 16 * kThreads == kTileBytes, "tile must split evenly over threads");
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kTileBytes];  // [stage][K, V]
+  static_assert(BC == 32 || BC == 64, "key tile");
+  constexpr int kBc = BC;
+  constexpr int NB = BC / 32;  // 32-key score blocks per tile
+  using L = TileLayout<D, BC>;
+  constexpr int RB = L::kRowBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[L::kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;  // query within the wave's 32-row block
   const int hi = lane >> 5;   // which half of the wave
 
@@ -106,14 +187,63 @@ void attn_fwd_kernel(const Params p) {
   int qt = g - bh * p.n_qtiles;
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // longest tiles first
   const int N = p.N;
+  const float c = p.c;
   const size_t head = (size_t)bh * (size_t)N * D;
   const __bf16* Qh = p.q + head;
-  const __bf16* Kh = p.k + head;
-  const __bf16* Vh = p.v + head;
 
   const int q0 = qt * kBr + wave * kQW;  // first query row of this wave
   const int qrow = q0 + col;
   const bool wave_active = q0 < N;
+
+  // ---- key range: the workgroup streams tiles up to its last query (causal) or N;
+  // each wave computes only the tiles that hold keys visible to its rows.
+  const int wg_kv_end = CAUSAL ? min(N, (qt + 1) * kBr) : N;
+  const int ntiles = (wg_kv_end + kBc - 1) / kBc;
+  const int wave_tiles = !wave_active ? 0 : CAUSAL ? (min(N, q0 + kQW) + kBc - 1) / kBc : ntiles;
+
+  // ---- K/V copies. Copy i of wave w fills tile rows (4w + i)*kRowsPerCopy + lane/kChunks
+  // (D = 128: 4 rows; D = 64: 8 rows), lane l writing physical chunk l % kChunks, so it
+  // fetches the logical chunk stored there. The per-lane source offsets inside a tile are
+  // fixed; the tile start is the scalar offset. In a ragged last tile, rows at or past N
+  // repeat key N-1 (finite data that receives probability 0), so no read leaves the tensor.
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const i32x4 krsrc = make_rsrc(p.k + head, head_bytes);
+  const i32x4 vrsrc = make_rsrc(p.v + head, head_bytes);
+  // Copy i starts 1 KiB after copy i-1 in both LDS and the source, and its rows differ by
+  // kRowsPerCopy (4 or 8): the chunk permutation repeats every 8 rows, so copy i's lane
+  // offsets are copy (i % kPeriod)'s plus (i / kPeriod) * kPeriod KiB.
+  constexpr int kPeriod = 8 / L::kRowsPerCopy < L::kCopies ? 8 / L::kRowsPerCopy : L::kCopies;
+  uint32_t coff[kPeriod];
+#pragma unroll
+  for (int i = 0; i < kPeriod; ++i) {
+    const int row = (wave * L::kCopies + i) * L::kRowsPerCopy + lane / L::kChunks;
+    coff[i] = row * RB + (((lane % L::kChunks) ^ swz(row & 7)) << 4);
+  }
+  const uint32_t smem_lds = lds_address(smem);
+  auto copy_tile = [&](const i32x4& rsrc, int t, uint32_t dst) {
+    const int key0 = t * kBc;
+    const uint32_t dst_w = dst + wave * L::kCopies * 1024;
+    if (key0 + kBc <= N) {
+#pragma unroll
+      for (int i = 0; i < L::kCopies; ++i) {
+        const uint32_t soff = __builtin_amdgcn_readfirstlane(key0 * RB + (i / kPeriod) * kPeriod * 1024);
+        copy16_to_lds(rsrc, coff[i % kPeriod], soff, dst_w + i * 1024);
+      }
+    } else {
+      // ragged last tile: rows at or past N - key0 repeat the last key
+      const uint32_t last = (uint32_t)(N - key0 - 1);
+      const uint32_t soff = __builtin_amdgcn_readfirstlane(key0 * RB);
+#pragma unroll
+      for (int i = 0; i < L::kCopies; ++i) {
+        const uint32_t o = coff[i % kPeriod] + (i / kPeriod) * kPeriod * 1024;
+        copy16_to_lds(rsrc, (min(o / RB, last) * RB) | (o % RB), soff, dst_w + i * 1024);
+      }
+    }
+  };
+  const uint32_t kbuf_lds[2] = {smem_lds, smem_lds + L::kTileBytes};
+  const uint32_t vbuf_lds[2] = {smem_lds + 2 * L::kTileBytes, smem_lds + 3 * L::kTileBytes};
+
+  copy_tile(krsrc, 0, kbuf_lds[0]);
 
   // ---- Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16s + 8hi .. +7]
   bf16x8 qf[D / 16];
@@ -126,135 +256,160 @@ void attn_fwd_kernel(const Params p) {
     for (int s = 0; s < D / 16; ++s) qf[s] = bf16x8{};
   }
 
-  // ---- key range: the workgroup loads tiles up to its last query (causal) or N
-  const int wg_kv_end = CAUSAL ? min(N, (qt + 1) * kBr) : N;
-  const int ntiles = (wg_kv_end + kBc - 1) / kBc;
-  const int wave_kv_end = CAUSAL ? min(N, q0 + kQW) : N;
-
-  u32x4 kst[kLoads], vst[kLoads];
-  auto load_tile = [&](int t) {
-    const int key0 = t * kBc;
+  // ---- per-lane LDS read bases
+  // K (A operand of S^T = K Q^T): lane (m + 32h) reads logical chunk 2st + h of row
+  // 32j + m. With st = 4a + b, its physical byte offset in the row is
+  // 128a + 32(b ^ (m & 3)) + 16(h ^ ((m >> 2) & 1)); k_base[b] holds all but 128a + row.
+  int k_base[4];
 #pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      const int ci = tid + u * kThreads;
-      const int r = ci / kChunks;
-      const int c = ci % kChunks;
-      const int key = key0 + r;
-      if (key < N) {
-        kst[u] = *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D + c * 8);
-        vst[u] = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + c * 8);
-      } else {
-        kst[u] = u32x4{0u, 0u, 0u, 0u};  // zero rows: finite, and masked to -inf anyway
-        vst[u] = u32x4{0u, 0u, 0u, 0u};
+  for (int b = 0; b < 4; ++b) k_base[b] = col * RB + 32 * (b ^ (col & 3)) + 16 * (hi ^ ((col >> 2) & 1));
+  // V^T (A operand of O^T = V^T P^T) through ds_read_b64_tr_b16: in each 16-lane group
+  // the source lane jj supplies 8 bytes of row 16st + 8u + 4h + (jj >> 2) at logical column
+  // 32d + 16(grp & 1) + 4(jj & 3); the instruction hands lane jj column jj of that 4-row
+  // block, so lane l ends up with V[4 consecutive keys][d = 32d + l % 32]. Physically the
+  // chunk is 8(d >> 1) + 4((d & 1) ^ jq1) + 2((grp & 1) ^ jq0) + (e ^ h) with jq = jj >> 2
+  // and e = (jj >> 1) & 1; v_base[d & 1] holds everything but 128(d >> 1) and the row.
+  const int jj = lane & 15;
+  const int grp = lane >> 4;
+  const int jq = jj >> 2;
+  int v_base[2];
+#pragma unroll
+  for (int e0 = 0; e0 < 2; ++e0)
+    v_base[e0] = (4 * hi + jq) * RB + 64 * (e0 ^ (jq >> 1)) + 32 * ((grp & 1) ^ (jq & 1)) +
+                 16 * (((jj >> 1) & 1) ^ hi) + 8 * (jj & 1);
+
+  // S^T (two 32-key x 32-query blocks) of the K tile at LDS offset kb
+  auto qk = [&](int kb, f32x16 (&s)[NB]) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      s[j] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const char* a = smem + kb + k_base[st & 3] + 32 * j * RB + 128 * (st >> 2);
+        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a), qf[st],
+                                                       s[j], 0, 0, 0);
       }
     }
   };
-  auto store_tile = [&](int stage) {
-    char* kb = smem + stage * 2 * kTileBytes;
-    char* vb = kb + kTileBytes;
-#pragma unroll
-    for (int u = 0; u < kLoads; ++u) {
-      const int ci = tid + u * kThreads;
-      const int off = lds_offset<D>(ci / kChunks, ci % kChunks);
-      *reinterpret_cast<u32x4*>(kb + off) = kst[u];
-      *reinterpret_cast<u32x4*>(vb + off) = vst[u];
-    }
-  };
 
-  // ---- per-lane pieces of the V^T transposing read (see the header comment)
-  const int jj = lane & 15;
-  const int grp = lane >> 4;
-  const int tr_row = 4 * hi + (jj >> 2);                       // + 16*step (+8 for keys 8..15)
-  const int tr_chunk = 2 * (grp & 1) + ((jj & 3) >> 1);       // + 4*db
-  const int tr_byte = (jj & 1) * 8;
-
-  float m = -INFINITY;  // running max of raw scores for query qrow
+  float m = -INFINITY;  // running max (raw scores) used by the exponentials of query qrow
   float l = 0.f;        // running sum of exp2(c*s - c*m) over this lane's keys
   f32x16 o[D / 32];
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) o[d] = f32x16{};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 1 < ntiles) load_tile(t + 1);
+  // Masking of tile t: keys past N and, causal, keys after the query. Only a wave's last
+  // tile can need it: a wave's rows span 32 queries and tiles 64 keys, so every earlier
+  // tile ends before the wave's first query, and only the last tile can pass N.
+  auto mask_tile = [&](f32x16 (&s)[NB], int t) {
     const int key0 = t * kBc;
-    if (wave_active && key0 < wave_kv_end) {
-      const char* kb = smem + (t & 1) * 2 * kTileBytes;
-      const char* vb = kb + kTileBytes;
-      // S^T = K Q^T for two 32-key blocks
-      f32x16 s[2];
+    if ((key0 + kBc > N) || (CAUSAL && key0 + kBc - 1 > q0)) {
+      // register r of block j holds key key0 + 4*hi + (32j + 8(r/4) + r%4); it is visible
+      // iff that key is < N and, causal, <= qrow
+      const int limit = (CAUSAL ? min(N, qrow + 1) : N) - key0 - 4 * hi;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        s[j] = f32x16{};
-        const int r = 32 * j + col;
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + lds_offset<D>(r, 2 * st + hi));
-          s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[j], 0, 0, 0);
-        }
-      }
-      // mask: keys past N (ragged last tile) and, causal, keys after the query
-      const bool need_mask = (key0 + kBc > N) || (CAUSAL && key0 + kBc - 1 > q0);
-      if (need_mask) {
+        for (int r = 0; r < 16; ++r)
+          if (32 * j + 8 * (r >> 2) + (r & 3) >= limit) s[j][r] = -INFINITY;
+    }
+  };
+  // row max and (lazy) rescale of tile t; leaves the scores in s
+  auto softmax_head = [&](f32x16 (&s)[NB]) {
+    float mx = m;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * j + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= N || (CAUSAL && key > qrow)) s[j][r] = -INFINITY;
-          }
-        }
-      }
-      // online softmax: new running max, rescale factor, exponentials
-      float mx = m;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
-      mx = max_across_halves(mx);
-      const float mc = mx * p.c;
-      const float alpha = __builtin_amdgcn_exp2f(m * p.c - mc);  // 0 on the first tile
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
+    mx = max_across_halves(mx);
+    // Lazy rescale: keep the old max unless some row's max grew by more than a factor
+    // 2^8 in probability. Exponentials then stay <= 256, and the final O / l uses the
+    // same max in numerator and denominator, so the result is unchanged.
+    if (__builtin_amdgcn_ballot_w64((mx - m) * c > kRescaleLog2)) {
+      const float alpha = __builtin_amdgcn_exp2f((m - mx) * c);  // 0 on the first tile
       m = mx;
-      float rs = 0.f;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][r], p.c, -mc));
-          s[j][r] = e;
-          rs += e;
-        }
-      l = l * alpha + rs;
+      l *= alpha;
 #pragma unroll
       for (int d = 0; d < D / 32; ++d)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-      // O^T += V^T P^T, 16 keys per MFMA step
+    }
+  };
+  // exponentials of tile t (after softmax_head), then O^T += V^T P^T with the V tile at
+  // LDS offset vb
+  auto exp_pv = [&](const f32x16 (&s)[NB], int vb) {
+    const float mc = m * c;
+    float rs = 0.f;
+    bf16x8 pb[2 * NB];
 #pragma unroll
-      for (int st = 0; st < kBc / 16; ++st) {
-        const int j = st >> 1;
-        const int h8 = (st & 1) * 8;
-        bf16x8 pb;
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = (__bf16)s[j][h8 + i];
-        const int row = 16 * st + tr_row;
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][r], c, -mc));
+        rs += e;
+        pb[2 * j + (r >> 3)][r & 7] = (__bf16)e;
+      }
+    l += rs;
+    // step st covers keys 16st..16st+15: lane half h holds keys 16st+4h+{0..3} (low four
+    // k positions) and 16st+8+4h+{0..3} (high four), matching pb[st]
 #pragma unroll
-        for (int d = 0; d < D / 32; ++d) {
-          const int chunk = 4 * d + tr_chunk;
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4*)(vb + lds_offset<D>(row, chunk) + tr_byte));
-          const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (lds_bf16x4*)(vb + lds_offset<D>(row + 8, chunk) + tr_byte));
-          const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[d], 0, 0, 0);
-        }
+    for (int st = 0; st < kBc / 16; ++st) {
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) {
+        const char* a0 = smem + vb + v_base[d & 1] + 16 * st * RB + 128 * (d >> 1);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a0);
+        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
+        const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[d], 0, 0, 0);
       }
     }
-    if (t + 1 < ntiles) store_tile((t + 1) & 1);
-    __syncthreads();
+  };
+
+  // ---- pipeline: the K ring runs one tile ahead of the V ring, so the scores of tile
+  // t+1 are formed while tile t goes through the exponentials and the P V product.
+  constexpr int kK0 = 0, kK1 = L::kTileBytes, kV0 = 2 * L::kTileBytes, kV1 = 3 * L::kTileBytes;
+  f32x16 sa[NB], sb[NB];
+  wait_copies_and_barrier();
+  if (wave_tiles > 0) qk(kK0, sa);
+  if (ntiles > 1) copy_tile(krsrc, 1, kbuf_lds[1]);
+  copy_tile(vrsrc, 0, vbuf_lds[0]);
+  wait_copies_and_barrier();
+
+  // Every iteration t issues the copies of K(t+2) and V(t+1) and ends with one barrier;
+  // all waves of the workgroup run ntiles iterations. A wave computes its tiles
+  // 0..wave_tiles-1 (a causal wave stops at its diagonal): steady steps while a next tile
+  // exists, then a last step, then barrier-only iterations.
+  auto copies = [&](int t) {
+    if (t + 2 < ntiles) copy_tile(krsrc, t + 2, kbuf_lds[t & 1]);
+    if (t + 1 < ntiles) copy_tile(vrsrc, t + 1, vbuf_lds[(t + 1) & 1]);
+  };
+  auto steady = [&](f32x16 (&cur)[NB], f32x16 (&nxt)[NB], int t) {
+    copies(t);
+    softmax_head(cur);
+    qk((t & 1) ? kK0 : kK1, nxt);
+    exp_pv(cur, (t & 1) ? kV1 : kV0);
+    interleave_schedule<D, BC>();
+    wait_copies_and_barrier();
+  };
+  auto last = [&](f32x16 (&cur)[NB], int t) {
+    copies(t);
+    mask_tile(cur, t);
+    softmax_head(cur);
+    exp_pv(cur, (t & 1) ? kV1 : kV0);
+    wait_copies_and_barrier();
+  };
+  int t = 0;
+  if (wave_tiles > 0) {
+    while (true) {
+      if (t + 1 >= wave_tiles) { last(sa, t); ++t; break; }
+      steady(sa, sb, t); ++t;
+      if (t + 1 >= wave_tiles) { last(sb, t); ++t; break; }
+      steady(sb, sa, t); ++t;
+    }
+  }
+  for (; t < ntiles; ++t) {
+    copies(t);
+    wait_copies_and_barrier();
   }
 
   // ---- epilogue: O / l in bf16 (round to nearest even), lse = ln 2 * (c*m + log2 l)
@@ -272,9 +427,27 @@ void attn_fwd_kernel(const Params p) {
           for (int i = 0; i < 4; ++i) w[i] = (__bf16)(o[d][4 * j4 + i] * inv);
           *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * j4 + 4 * hi) = w;
         }
-      if (hi == 0) p.lse[(size_t)bh * N + qrow] = (m * p.c + __builtin_log2f(lt)) * kLn2;
+      if (hi == 0) p.lse[(size_t)bh * N + qrow] = (m * c + __builtin_log2f(lt)) * kLn2;
     }
   }
+}
+
+template <int D, int BC>
+void launch(int causal, dim3 grid, dim3 block, hipStream_t s, const Params& p) {
+  if (causal) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, false>), grid, block, 0, s, p);
+}
+
+// Keys per K/V tile for head dimension D. ATTN_FWD_BC (32 or 64), read once, overrides
+// the default for tuning experiments.
+int key_tile(int D) {
+  static const int forced = [] {
+    const char* e = getenv("ATTN_FWD_BC");
+    const int v = e ? atoi(e) : 0;
+    return (v == 32 || v == 64) ? v : 0;
+  }();
+  if (forced) return forced;
+  return D == 128 ? 32 : 64;
 }
 
 }  // namespace
@@ -318,12 +491,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid_dim((unsigned)grid), block_dim(kThreads);
+  const int bc = key_tile(D);
   if (D == 64) {
-    if (causal) hipLaunchKernelGGL((attn_fwd_kernel<64, true>), grid_dim, block_dim, 0, s, p);
-    else hipLaunchKernelGGL((attn_fwd_kernel<64, false>), grid_dim, block_dim, 0, s, p);
+    if (bc == 32) launch<64, 32>(causal, grid_dim, block_dim, s, p);
+    else launch<64, 64>(causal, grid_dim, block_dim, s, p);
   } else {
-    if (causal) hipLaunchKernelGGL((attn_fwd_kernel<128, true>), grid_dim, block_dim, 0, s, p);
-    else hipLaunchKernelGGL((attn_fwd_kernel<128, false>), grid_dim, block_dim, 0, s, p);
+    if (bc == 32) launch<128, 32>(causal, grid_dim, block_dim, s, p);
+    else launch<128, 64>(causal, grid_dim, block_dim, s, p);
   }
   if (hipGetLastError() != hipSuccess) return ATTN_FWD_ELAUNCH;
   return ATTN_FWD_OK;
