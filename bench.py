@@ -87,6 +87,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 512 MiB device-to-device copy (3 times) so that "
+                         "hardware byte counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -175,6 +178,15 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 3 x 512 MiB device-to-device")
+        del src, dst
     if not args.no_cpu_baseline:
         log(f"[bench] timing the fp64 oracle on host cores (~{args.cpu_seconds:.0f} s budget)")
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)

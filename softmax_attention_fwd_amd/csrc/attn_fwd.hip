@@ -51,6 +51,7 @@ constexpr int kQW = 32;              // query rows per wave
 constexpr int kBr = kWaves * kQW;    // query rows per workgroup
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.44269504088896341f;
+constexpr int kWaitVmcnt0 = 0x0F70;    // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold, in log2 units of probability
 
 struct Params {
@@ -77,16 +78,31 @@ __device__ inline float sum_across_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS tile layout. A K or V tile is BC rows (keys) of D bf16, row-major, unpadded; its
-// 16-byte chunks are permuted within each row: logical chunk c of row r is stored at
-// physical chunk c ^ f(r & 7), with f(r) = ((r & 3) << 1) | ((r >> 2) & 1) (a 3-bit
-// rotation). f is a bijection on any 8 aligned rows, so the score MFMA's K reads (eight
-// lanes reading one chunk of eight consecutive rows) hit eight different bank groups, and
-// on any 4 aligned rows f >> 1 is distinct, so each 16-lane group of the transposing V read
-// (two adjacent chunks of four consecutive rows) also covers eight different bank groups.
-// Splitting the XOR into bit fields, every read address is one of a few per-lane bases
-// plus a compile-time offset (see k_base / v_base in the kernel).
-__device__ inline int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// LDS tile layout. A K or V tile is BC rows (keys) of D bf16, row-major and unpadded; the
+// 16-byte chunks of each row are permuted: logical chunk c of row r sits at physical chunk
+// c ^ f(r). The LDS has 64 four-byte banks; a 16-byte-per-lane read is serviced 16 lanes
+// at a time and an 8-byte one (including ds_read_b64_tr_b16) 32 lanes at a time, so a
+// conflict-free read must spread each such lane group over all 64 banks.
+//  * K tile (score MFMA A operand): 16 consecutive lanes read one logical chunk of 16
+//    consecutive rows, so f must be a bijection on the rows' bank groups: for D = 128
+//    (256-byte rows) f = 4(r & 3) + ((r >> 2) & 3) over r mod 16; for D = 64 (128-byte
+//    rows, two per bank line) a 3-bit rotation of (r >> 1) & 7.
+//  * V tile (transposing read): 32 lanes read two adjacent chunks (four 8-byte quarters)
+//    of four consecutive rows, twice; f only has to separate those four rows in the chunk
+//    bits above the two that vary: f = 4(r & 3) for D = 128, 4((r >> 1) & 1) for D = 64.
+// With these choices every read address is a per-lane base (one per K step, one per V
+// column block) plus a compile-time offset.
+template <int D>
+__device__ inline int swz_k(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  const int a = (r >> 1) & 7;
+  return ((a & 1) << 2) | (a >> 1);
+}
+template <int D>
+__device__ inline int swz_v(int r) {
+  if constexpr (D == 128) return (r & 3) << 2;
+  return ((r >> 1) & 1) << 2;
+}
 
 template <int D, int BC>
 struct TileLayout {
@@ -97,29 +113,32 @@ struct TileLayout {
   static constexpr int kCopies = kTileBytes / 1024 / kWaves;  // copies per wave per tile
   static constexpr int kLdsBytes = 4 * kTileBytes;         // K[2], V[2]
   static_assert(kCopies * 1024 * kWaves == kTileBytes, "tile must split into 1 KiB copies per wave");
-  static_assert(kChunks >= 8, "the chunk permutation needs 8 chunks per row");
+  static_assert(kChunks >= 8, "the chunk permutations need 8 chunks per row");
+  // copies whose lane offsets differ (the permutations repeat every 16 / 4 rows)
+  static constexpr int kPeriodK = 16 / kRowsPerCopy < kCopies ? 16 / kRowsPerCopy : kCopies;
+  static constexpr int kPeriodV = 4 / kRowsPerCopy < 1 ? 1 : (4 / kRowsPerCopy < kCopies ? 4 / kRowsPerCopy : kCopies);
 };
 
 // Instruction order for the steady-state block "scores of tile t+1 || exponentials of
-// tile t, then O += P V of tile t": each score MFMA is paired with its LDS operand read
-// and a share of the exponential work, then each P V MFMA with its two transposing reads.
-// This keeps the matrix cores busy while the VALU works and bounds the operand registers
-// in flight.
+// tile t, then O += P V of tile t": each score MFMA is paired with a share of the
+// exponential work, then the P V MFMAs follow. LDS reads run two MFMAs ahead of the MFMA
+// that consumes them, so their latency is hidden behind the matrix core.
 template <int D, int BC>
 __device__ inline void interleave_schedule() {
   constexpr int kQkMfma = (BC / 32) * (D / 16);
   constexpr int kPvMfma = (BC / 16) * (D / 32);
   constexpr int kValu = 56 * (BC / 32);  // exponential work of the tile, roughly
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // K reads for the first two MFMAs
 #pragma unroll
   for (int i = 0; i < kQkMfma; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // next DS read
     __builtin_amdgcn_sched_group_barrier(0x002, kValu / kQkMfma, 0);  // VALU
   }
 #pragma unroll
   for (int i = 0; i < kPvMfma; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (transposing)
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // transposing reads, two ahead
     __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
   }
 }
@@ -138,9 +157,12 @@ __device__ inline i32x4 make_rsrc(const void* base, uint32_t num_bytes) {
 
 // One 16-byte-per-lane copy global -> LDS (buffer_load_dwordx4 ... lds): lane l reads
 // rsrc.base + soff + voff[l] and writes LDS address lds + 16*l. The copy is asynchronous
-// (counted by vmcnt); wait_copies_and_barrier() completes it. It is issued from inline
-// assembly so that the compiler does not serialise unrelated LDS reads behind it; M0 is
-// used by nothing else in these kernels.
+// (counted by vmcnt); the explicit waits before the barriers complete it. It is issued
+// from inline assembly, without a memory clobber, so that the compiler neither makes
+// unrelated LDS reads wait for it nor treats it as ordered with them: every copy targets
+// a ring slot that no wave reads until after the next barrier, and the reads of that
+// slot's previous contents all precede the barrier before the copy. M0 is used by
+// nothing else in these kernels.
 __device__ inline void copy16_to_lds(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %3\n\t"
@@ -148,7 +170,7 @@ __device__ inline void copy16_to_lds(i32x4 rsrc, uint32_t voff, uint32_t soff, u
       "buffer_load_dwordx4 %0, %1, %2 offen lds"
       :
       : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
-      : "memory", "m0");
+      : "m0");
 }
 
 __device__ inline void wait_copies_and_barrier() {
@@ -209,25 +231,29 @@ void attn_fwd_kernel(const Params p) {
   const uint32_t head_bytes = (uint32_t)N * RB;
   const i32x4 krsrc = make_rsrc(p.k + head, head_bytes);
   const i32x4 vrsrc = make_rsrc(p.v + head, head_bytes);
-  // Copy i starts 1 KiB after copy i-1 in both LDS and the source, and its rows differ by
-  // kRowsPerCopy (4 or 8): the chunk permutation repeats every 8 rows, so copy i's lane
-  // offsets are copy (i % kPeriod)'s plus (i / kPeriod) * kPeriod KiB.
-  constexpr int kPeriod = 8 / L::kRowsPerCopy < L::kCopies ? 8 / L::kRowsPerCopy : L::kCopies;
-  uint32_t coff[kPeriod];
+  // Copy i starts 1 KiB after copy i-1 in both LDS and the source and covers rows
+  // kRowsPerCopy further on; the permutations repeat every 16 (K) or 4 (V) rows, so copy
+  // i's lane offsets are those of copy i % kPeriod plus (i / kPeriod) * kPeriod KiB.
+  uint32_t koff[L::kPeriodK], voff[L::kPeriodV];
 #pragma unroll
-  for (int i = 0; i < kPeriod; ++i) {
+  for (int i = 0; i < L::kPeriodK; ++i) {
     const int row = (wave * L::kCopies + i) * L::kRowsPerCopy + lane / L::kChunks;
-    coff[i] = row * RB + (((lane % L::kChunks) ^ swz(row & 7)) << 4);
+    koff[i] = row * RB + (((lane % L::kChunks) ^ swz_k<D>(row)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < L::kPeriodV; ++i) {
+    const int row = (wave * L::kCopies + i) * L::kRowsPerCopy + lane / L::kChunks;
+    voff[i] = row * RB + (((lane % L::kChunks) ^ swz_v<D>(row)) << 4);
   }
   const uint32_t smem_lds = lds_address(smem);
-  auto copy_tile = [&](const i32x4& rsrc, int t, uint32_t dst) {
+  auto copy_tile = [&](const i32x4& rsrc, const uint32_t* coff, int period, int t, uint32_t dst) {
     const int key0 = t * kBc;
     const uint32_t dst_w = dst + wave * L::kCopies * 1024;
     if (key0 + kBc <= N) {
 #pragma unroll
       for (int i = 0; i < L::kCopies; ++i) {
-        const uint32_t soff = __builtin_amdgcn_readfirstlane(key0 * RB + (i / kPeriod) * kPeriod * 1024);
-        copy16_to_lds(rsrc, coff[i % kPeriod], soff, dst_w + i * 1024);
+        const uint32_t soff = __builtin_amdgcn_readfirstlane(key0 * RB + (i / period) * period * 1024);
+        copy16_to_lds(rsrc, coff[i % period], soff, dst_w + i * 1024);
       }
     } else {
       // ragged last tile: rows at or past N - key0 repeat the last key
@@ -235,7 +261,7 @@ void attn_fwd_kernel(const Params p) {
       const uint32_t soff = __builtin_amdgcn_readfirstlane(key0 * RB);
 #pragma unroll
       for (int i = 0; i < L::kCopies; ++i) {
-        const uint32_t o = coff[i % kPeriod] + (i / kPeriod) * kPeriod * 1024;
+        const uint32_t o = coff[i % period] + (i / period) * period * 1024;
         copy16_to_lds(rsrc, (min(o / RB, last) * RB) | (o % RB), soff, dst_w + i * 1024);
       }
     }
@@ -243,7 +269,9 @@ void attn_fwd_kernel(const Params p) {
   const uint32_t kbuf_lds[2] = {smem_lds, smem_lds + L::kTileBytes};
   const uint32_t vbuf_lds[2] = {smem_lds + 2 * L::kTileBytes, smem_lds + 3 * L::kTileBytes};
 
-  copy_tile(krsrc, 0, kbuf_lds[0]);
+  auto copy_k = [&](int t, uint32_t dst) { copy_tile(krsrc, koff, L::kPeriodK, t, dst); };
+  auto copy_v = [&](int t, uint32_t dst) { copy_tile(vrsrc, voff, L::kPeriodV, t, dst); };
+  copy_k(0, kbuf_lds[0]);
 
   // ---- Q as the B operand of S^T = K Q^T: lane holds Q[qrow][16s + 8hi .. +7]
   bf16x8 qf[D / 16];
@@ -255,28 +283,30 @@ void attn_fwd_kernel(const Params p) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qf[s] = bf16x8{};
   }
+  // Complete the Q loads here, visibly to the compiler (vmcnt(0)): otherwise it keeps them
+  // pending into the main loop and waits on vmcnt there, i.e. on the K/V copies in flight.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   // ---- per-lane LDS read bases
   // K (A operand of S^T = K Q^T): lane (m + 32h) reads logical chunk 2st + h of row
-  // 32j + m. With st = 4a + b, its physical byte offset in the row is
-  // 128a + 32(b ^ (m & 3)) + 16(h ^ ((m >> 2) & 1)); k_base[b] holds all but 128a + row.
-  int k_base[4];
+  // 32j + m; the permutation depends on m only, so k_addr[st] covers every j and buffer.
+  int k_addr[D / 16];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) k_base[b] = col * RB + 32 * (b ^ (col & 3)) + 16 * (hi ^ ((col >> 2) & 1));
+  for (int st = 0; st < D / 16; ++st) k_addr[st] = col * RB + 16 * ((2 * st + hi) ^ swz_k<D>(col));
   // V^T (A operand of O^T = V^T P^T) through ds_read_b64_tr_b16: in each 16-lane group
   // the source lane jj supplies 8 bytes of row 16st + 8u + 4h + (jj >> 2) at logical column
   // 32d + 16(grp & 1) + 4(jj & 3); the instruction hands lane jj column jj of that 4-row
-  // block, so lane l ends up with V[4 consecutive keys][d = 32d + l % 32]. Physically the
-  // chunk is 8(d >> 1) + 4((d & 1) ^ jq1) + 2((grp & 1) ^ jq0) + (e ^ h) with jq = jj >> 2
-  // and e = (jj >> 1) & 1; v_base[d & 1] holds everything but 128(d >> 1) and the row.
+  // block, so lane l ends up with V[4 consecutive keys][32d + l % 32]. The permutation
+  // depends on (jj >> 2) and h only, so v_addr[d] covers every st, u and buffer.
   const int jj = lane & 15;
   const int grp = lane >> 4;
-  const int jq = jj >> 2;
-  int v_base[2];
+  int v_addr[D / 32];
 #pragma unroll
-  for (int e0 = 0; e0 < 2; ++e0)
-    v_base[e0] = (4 * hi + jq) * RB + 64 * (e0 ^ (jq >> 1)) + 32 * ((grp & 1) ^ (jq & 1)) +
-                 16 * (((jj >> 1) & 1) ^ hi) + 8 * (jj & 1);
+  for (int d = 0; d < D / 32; ++d) {
+    const int row = 4 * hi + (jj >> 2);
+    const int chunk = 4 * d + 2 * (grp & 1) + ((jj >> 1) & 1);
+    v_addr[d] = row * RB + 16 * (chunk ^ swz_v<D>(row)) + 8 * (jj & 1);
+  }
 
   // S^T (two 32-key x 32-query blocks) of the K tile at LDS offset kb
   auto qk = [&](int kb, f32x16 (&s)[NB]) {
@@ -285,7 +315,7 @@ void attn_fwd_kernel(const Params p) {
       s[j] = f32x16{};
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        const char* a = smem + kb + k_base[st & 3] + 32 * j * RB + 128 * (st >> 2);
+        const char* a = smem + kb + k_addr[st] + 32 * j * RB;
         s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a), qf[st],
                                                        s[j], 0, 0, 0);
       }
@@ -356,7 +386,7 @@ void attn_fwd_kernel(const Params p) {
     for (int st = 0; st < kBc / 16; ++st) {
 #pragma unroll
       for (int d = 0; d < D / 32; ++d) {
-        const char* a0 = smem + vb + v_base[d & 1] + 16 * st * RB + 128 * (d >> 1);
+        const char* a0 = smem + vb + v_addr[d] + 16 * st * RB;
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a0);
         const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
         const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -371,8 +401,8 @@ void attn_fwd_kernel(const Params p) {
   f32x16 sa[NB], sb[NB];
   wait_copies_and_barrier();
   if (wave_tiles > 0) qk(kK0, sa);
-  if (ntiles > 1) copy_tile(krsrc, 1, kbuf_lds[1]);
-  copy_tile(vrsrc, 0, vbuf_lds[0]);
+  if (ntiles > 1) copy_k(1, kbuf_lds[1]);
+  copy_v(0, vbuf_lds[0]);
   wait_copies_and_barrier();
 
   // Every iteration t issues the copies of K(t+2) and V(t+1) and ends with one barrier;
@@ -380,8 +410,8 @@ void attn_fwd_kernel(const Params p) {
   // 0..wave_tiles-1 (a causal wave stops at its diagonal): steady steps while a next tile
   // exists, then a last step, then barrier-only iterations.
   auto copies = [&](int t) {
-    if (t + 2 < ntiles) copy_tile(krsrc, t + 2, kbuf_lds[t & 1]);
-    if (t + 1 < ntiles) copy_tile(vrsrc, t + 1, vbuf_lds[(t + 1) & 1]);
+    if (t + 2 < ntiles) copy_k(t + 2, kbuf_lds[t & 1]);
+    if (t + 1 < ntiles) copy_v(t + 1, vbuf_lds[(t + 1) & 1]);
   };
   auto steady = [&](f32x16 (&cur)[NB], f32x16 (&nxt)[NB], int t) {
     copies(t);
@@ -398,14 +428,20 @@ void attn_fwd_kernel(const Params p) {
     exp_pv(cur, (t & 1) ? kV1 : kV0);
     wait_copies_and_barrier();
   };
+  // Pairs of steady steps keep the scores of the current tile in sa at every trip of the
+  // loop, so the accumulators keep their registers from one trip to the next.
   int t = 0;
-  if (wave_tiles > 0) {
-    while (true) {
-      if (t + 1 >= wave_tiles) { last(sa, t); ++t; break; }
-      steady(sa, sb, t); ++t;
-      if (t + 1 >= wave_tiles) { last(sb, t); ++t; break; }
-      steady(sb, sa, t); ++t;
-    }
+  for (; t + 2 < wave_tiles; t += 2) {
+    steady(sa, sb, t);
+    steady(sb, sa, t + 1);
+  }
+  if (t + 1 < wave_tiles) {
+    steady(sa, sb, t);
+    last(sb, t + 1);
+    t += 2;
+  } else if (t < wave_tiles) {
+    last(sa, t);
+    t += 1;
   }
   for (; t < ntiles; ++t) {
     copies(t);
@@ -432,6 +468,359 @@ void attn_fwd_kernel(const Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Wide variant: one wave per SIMD, 64 query rows per wave as two independent 32-row blocks
+// (A and B), three-stage K/V rings (tiles of 32 keys for D = 128, 64 for D = 64). Every K or V fragment read from LDS feeds
+// one MFMA of each block, and while one block works through its exponentials the other
+// block's MFMAs keep the matrix core busy, so the VALU and MFMA work of a single wave
+// overlap. Up to 512 registers per wave (VGPR + AGPR).
+constexpr int kWideQW = 64;                 // query rows per wave (two 32-row blocks)
+constexpr int kWideBr = kWaves * kWideQW;   // 256 query rows per workgroup
+constexpr int kWideStages = 3;
+template <int D>
+constexpr int wide_bc() { return D == 128 ? 32 : 64; }  // keys per tile
+
+template <int D, int BC>
+__device__ inline void wide_schedule() {
+  // phase 1: (BC/32) x (D/16) score MFMA pairs (one K read each) || exponentials of both
+  // blocks (about 112 VALU instructions per block per 64 keys); reads two pairs ahead
+  constexpr int kQkReads = (BC / 32) * (D / 16);
+  constexpr int kValu = 112 * 2 * BC / 64;
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int i = 0; i < kQkReads; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                // MFMA (A, B)
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // next DS read (K)
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu / kQkReads, 0);  // VALU
+  }
+  // phase 2: P V MFMA pairs, their transposing reads two pairs ahead
+  constexpr int kPvReads = (BC / 16) * (D / 32);
+#pragma unroll
+  for (int i = 0; i < kPvReads; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA (A, B)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (V^T)
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_wide_kernel(const Params p) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  constexpr int BC = wide_bc<D>();
+  constexpr int NB = BC / 32;  // 32-key score blocks per tile
+  constexpr int QB = 2;        // 32-row query blocks per wave
+  using L = TileLayout<D, BC>;
+  constexpr int RB = L::kRowBytes;
+  constexpr int T = L::kTileBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kWideStages * T];  // K[3], V[3]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int hi = lane >> 5;
+
+  // ---- work unit
+  int g = blockIdx.x;
+  if (p.remap) {
+    const int per_xcd = gridDim.x >> 3;
+    g = (g & 7) * per_xcd + (g >> 3);
+  }
+  const int bh = g / p.n_qtiles;
+  int qt = g - bh * p.n_qtiles;
+  if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // longest tiles first
+  const int N = p.N;
+  const float c = p.c;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const __bf16* Qh = p.q + head;
+
+  const int q0 = qt * kWideBr + wave * kWideQW;  // first query row of this wave
+  const bool wave_active = q0 < N;
+  const int wg_kv_end = CAUSAL ? min(N, (qt + 1) * kWideBr) : N;
+  const int ntiles = (wg_kv_end + BC - 1) / BC;
+  const int wave_tiles = !wave_active ? 0 : CAUSAL ? (min(N, q0 + kWideQW) + BC - 1) / BC : ntiles;
+
+  // ---- K/V copies (same scheme as the narrow kernel; runtime ring slot in M0)
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const i32x4 krsrc = make_rsrc(p.k + head, head_bytes);
+  const i32x4 vrsrc = make_rsrc(p.v + head, head_bytes);
+  uint32_t koff[L::kPeriodK], voff[L::kPeriodV];
+#pragma unroll
+  for (int i = 0; i < L::kPeriodK; ++i) {
+    const int row = (wave * L::kCopies + i) * L::kRowsPerCopy + lane / L::kChunks;
+    koff[i] = row * RB + (((lane % L::kChunks) ^ swz_k<D>(row)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < L::kPeriodV; ++i) {
+    const int row = (wave * L::kCopies + i) * L::kRowsPerCopy + lane / L::kChunks;
+    voff[i] = row * RB + (((lane % L::kChunks) ^ swz_v<D>(row)) << 4);
+  }
+  const uint32_t smem_lds = lds_address(smem);
+  auto copy_tile = [&](const i32x4& rsrc, const uint32_t* coff, int period, int t, uint32_t dst) {
+    const int key0 = t * BC;
+    const uint32_t dst_w = dst + wave * L::kCopies * 1024;
+    if (key0 + BC <= N) {
+#pragma unroll
+      for (int i = 0; i < L::kCopies; ++i) {
+        const uint32_t soff = __builtin_amdgcn_readfirstlane(key0 * RB + (i / period) * period * 1024);
+        copy16_to_lds(rsrc, coff[i % period], soff, dst_w + i * 1024);
+      }
+    } else {
+      const uint32_t last = (uint32_t)(N - key0 - 1);
+      const uint32_t soff = __builtin_amdgcn_readfirstlane(key0 * RB);
+#pragma unroll
+      for (int i = 0; i < L::kCopies; ++i) {
+        const uint32_t o = coff[i % period] + (i / period) * period * 1024;
+        copy16_to_lds(rsrc, (min(o / RB, last) * RB) | (o % RB), soff, dst_w + i * 1024);
+      }
+    }
+  };
+  auto copy_k = [&](int t) { copy_tile(krsrc, koff, L::kPeriodK, t, smem_lds + (t % kWideStages) * T); };
+  auto copy_v = [&](int t) {
+    copy_tile(vrsrc, voff, L::kPeriodV, t, smem_lds + (kWideStages + t % kWideStages) * T);
+  };
+  // Wait for every copy except the `in_flight` most recent ones, then barrier.
+  auto wait_and_barrier = [&](int in_flight) {
+    if (in_flight == 2 * L::kCopies) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L::kCopies) : "memory");
+    else if (in_flight == L::kCopies) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L::kCopies) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  copy_k(0);
+  if (ntiles > 1) copy_k(1);
+  copy_v(0);
+
+  // ---- Q fragments of both blocks
+  bf16x8 qf[QB][D / 16];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const int qrow = q0 + 32 * b + col;
+    if (qrow < N) {
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D) + hi;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) qf[b][s] = src[2 * s];
+    } else {
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) qf[b][s] = bf16x8{};
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // see the narrow kernel
+
+  // ---- per-lane LDS read bases (as in the narrow kernel)
+  int k_addr[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) k_addr[st] = col * RB + 16 * ((2 * st + hi) ^ swz_k<D>(col));
+  const int jj = lane & 15;
+  const int grp = lane >> 4;
+  int v_addr[D / 32];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) {
+    const int row = 4 * hi + (jj >> 2);
+    const int chunk = 4 * d + 2 * (grp & 1) + ((jj >> 1) & 1);
+    v_addr[d] = row * RB + 16 * (chunk ^ swz_v<D>(row)) + 8 * (jj & 1);
+  }
+
+  // scores of both blocks for the K tile in ring slot ks (a constant in the unrolled main
+  // loop, so the slot offset folds into the read's immediate)
+  auto qk = [&](int ks, f32x16 (&s)[QB][NB]) {
+    const char* kb = smem + ks * T;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      s[0][j] = f32x16{};
+      s[1][j] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + k_addr[st] + 32 * j * RB);
+        s[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][st], s[0][j], 0, 0, 0);
+        s[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][st], s[1][j], 0, 0, 0);
+      }
+    }
+  };
+
+  float m[QB] = {-INFINITY, -INFINITY};
+  float l[QB] = {0.f, 0.f};
+  f32x16 o[QB][D / 32];
+#pragma unroll
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d) o[b][d] = f32x16{};
+
+  auto mask_tile = [&](f32x16 (&s)[QB][NB], int t) {
+    const int key0 = t * BC;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int qb0 = q0 + 32 * b;
+      if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qb0)) {
+        const int limit = (CAUSAL ? min(N, qb0 + col + 1) : N) - key0 - 4 * hi;
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * j + 8 * (r >> 2) + (r & 3) >= limit) s[b][j][r] = -INFINITY;
+      }
+    }
+  };
+  auto softmax_head = [&](f32x16 (&s)[QB][NB]) {
+    float mx[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      mx[b] = m[b];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx[b] = fmaxf(mx[b], s[b][j][r]);
+      mx[b] = max_across_halves(mx[b]);
+    }
+    // lazy rescale (see the narrow kernel); one decision for both blocks
+    if (__builtin_amdgcn_ballot_w64((mx[0] - m[0]) * c > kRescaleLog2 || (mx[1] - m[1]) * c > kRescaleLog2)) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        const float alpha = __builtin_amdgcn_exp2f((m[b] - mx[b]) * c);
+        m[b] = mx[b];
+        l[b] *= alpha;
+#pragma unroll
+        for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[b][d][r] *= alpha;
+      }
+    }
+  };
+  auto exp_pv = [&](int vs, const f32x16 (&s)[QB][NB]) {
+    const char* vb = smem + (kWideStages + vs) * T;
+    bf16x8 pb[QB][2 * NB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const float mc = m[b] * c;
+      float rs = 0.f;
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][j][r], c, -mc));
+          rs += e;
+          pb[b][2 * j + (r >> 3)][r & 7] = (__bf16)e;
+        }
+      l[b] += rs;
+    }
+#pragma unroll
+    for (int st = 0; st < BC / 16; ++st) {
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) {
+        const char* a0 = vb + v_addr[d] + 16 * st * RB;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a0);
+        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
+        const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[0][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][st], o[0][d], 0, 0, 0);
+        o[1][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][st], o[1][d], 0, 0, 0);
+      }
+    }
+  };
+
+  // copies of iteration t: K(t+3) and V(t+2); returns how many this wave issued
+  auto copies = [&](int t) {
+    int n = 0;
+    if (t + 3 < ntiles) { copy_k(t + 3); n += L::kCopies; }
+    if (t + 2 < ntiles) { copy_v(t + 2); n += L::kCopies; }
+    return n;
+  };
+
+  // ---- prologue: K(0), K(1), V(0) in flight; scores of tile 0; then K(2), V(1)
+  f32x16 sa[QB][NB], sb[QB][NB];
+  wait_and_barrier((ntiles > 1 ? L::kCopies : 0) + L::kCopies);  // K(0) landed
+  if (wave_tiles > 0) qk(0, sa);
+  {
+    int n = 0;
+    if (ntiles > 2) { copy_k(2); n += L::kCopies; }
+    if (ntiles > 1) { copy_v(1); n += L::kCopies; }
+    wait_and_barrier(n);  // K(1), V(0) landed
+  }
+
+  // iteration t: scores of tile t in cur; K(t+1) is in ring slot (t+1) % 3, V(t) in t % 3
+  auto steady = [&](int kslot, int vslot, f32x16 (&cur)[QB][NB], f32x16 (&nxt)[QB][NB], int t) {
+    const int n = copies(t);
+    softmax_head(cur);
+    qk(kslot, nxt);
+    exp_pv(vslot, cur);
+    wide_schedule<D, BC>();
+    wait_and_barrier(n);
+  };
+  auto last = [&](int vslot, f32x16 (&cur)[QB][NB], int t) {
+    const int n = copies(t);
+    mask_tile(cur, t);
+    softmax_head(cur);
+    exp_pv(vslot, cur);
+    wait_and_barrier(n);
+  };
+
+  // Main loop: six steps per trip (lcm of the two score buffers and the three ring slots),
+  // all slots compile-time constants. A wave's rows span kMaskTiles tiles, so only its last
+  // kMaskTiles tiles can hold its diagonal (causal) or the ragged end; the main loop stops
+  // before them, and the remaining tiles go through one runtime-slot loop that masks and
+  // copies the scores back into sa, so no other code path holds them elsewhere.
+  constexpr int kMaskTiles = (kWideQW + BC - 1) / BC;
+  auto steady_masked = [&](int kslot, int vslot, f32x16 (&cur)[QB][NB], f32x16 (&nxt)[QB][NB], int t) {
+    const int n = copies(t);
+    mask_tile(cur, t);
+    softmax_head(cur);
+    qk(kslot, nxt);
+    exp_pv(vslot, cur);
+    wide_schedule<D, BC>();
+    wait_and_barrier(n);
+  };
+  int t = 0;
+  for (; t + 5 + kMaskTiles < wave_tiles; t += 6) {
+    steady(1, 0, sa, sb, t);
+    steady(2, 1, sb, sa, t + 1);
+    steady(0, 2, sa, sb, t + 2);
+    steady(1, 0, sb, sa, t + 3);
+    steady(2, 1, sa, sb, t + 4);
+    steady(0, 2, sb, sa, t + 5);
+  }
+  for (; t + 1 < wave_tiles; ++t) {
+    steady_masked((t + 1) % kWideStages, t % kWideStages, sa, sb, t);
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) sa[b][j] = sb[b][j];
+  }
+  if (t < wave_tiles) {
+    last(t % kWideStages, sa, t);
+    ++t;
+  }
+  for (; t < ntiles; ++t) wait_and_barrier(copies(t));
+
+  // ---- epilogue
+  if (wave_active) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const float lt = sum_across_halves(l[b]);
+      const int qrow = q0 + 32 * b + col;
+      if (qrow < N) {
+        const float inv = 1.f / lt;
+        __bf16* orow = p.o + head + (size_t)qrow * D;
+#pragma unroll
+        for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+          for (int j4 = 0; j4 < 4; ++j4) {
+            bf16x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = (__bf16)(o[b][d][4 * j4 + i] * inv);
+            *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * j4 + 4 * hi) = w;
+          }
+        if (hi == 0) p.lse[(size_t)bh * N + qrow] = (m[b] * c + __builtin_log2f(lt)) * kLn2;
+      }
+    }
+  }
+}
+
+template <int D>
+void launch_wide(int causal, dim3 grid, dim3 block, hipStream_t s, const Params& p) {
+  if (causal) hipLaunchKernelGGL((attn_fwd_wide_kernel<D, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_fwd_wide_kernel<D, false>), grid, block, 0, s, p);
+}
+
 template <int D, int BC>
 void launch(int causal, dim3 grid, dim3 block, hipStream_t s, const Params& p) {
   if (causal) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, true>), grid, block, 0, s, p);
@@ -447,7 +836,20 @@ int key_tile(int D) {
     return (v == 32 || v == 64) ? v : 0;
   }();
   if (forced) return forced;
-  return D == 128 ? 32 : 64;
+  return 64;
+}
+
+// Kernel family: "wide" (64 rows per wave, one wave per SIMD) or "narrow" (32 rows per
+// wave, two waves per SIMD). ATTN_FWD_KERNEL, read once, overrides the default for tuning.
+bool use_wide_kernel() {
+  static const int forced = [] {
+    const char* e = getenv("ATTN_FWD_KERNEL");
+    if (!e) return -1;
+    if (e[0] == 'w') return 1;
+    if (e[0] == 'n') return 0;
+    return -1;
+  }();
+  return forced == 1;
 }
 
 }  // namespace
@@ -472,7 +874,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (causal != 0 && causal != 1) return ATTN_FWD_EINVAL;
   if (!(scale > 0.f) || !isfinite(scale)) return ATTN_FWD_EINVAL;
   if (D != 64 && D != 128) return ATTN_FWD_EUNSUPPORTED;
-  const int64_t n_qtiles = ((int64_t)N + kBr - 1) / kBr;
+  const bool wide = use_wide_kernel();
+  const int br = wide ? kWideBr : kBr;
+  const int64_t n_qtiles = ((int64_t)N + br - 1) / br;
   const int64_t grid = (int64_t)B * H * n_qtiles;
   if ((int64_t)N * D >= ((int64_t)1 << 31) || grid >= ((int64_t)1 << 31)) return ATTN_FWD_EINVAL;
   const uintptr_t a16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o;
@@ -491,13 +895,18 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid_dim((unsigned)grid), block_dim(kThreads);
-  const int bc = key_tile(D);
-  if (D == 64) {
-    if (bc == 32) launch<64, 32>(causal, grid_dim, block_dim, s, p);
-    else launch<64, 64>(causal, grid_dim, block_dim, s, p);
+  if (wide) {
+    if (D == 64) launch_wide<64>(causal, grid_dim, block_dim, s, p);
+    else launch_wide<128>(causal, grid_dim, block_dim, s, p);
   } else {
-    if (bc == 32) launch<128, 32>(causal, grid_dim, block_dim, s, p);
-    else launch<128, 64>(causal, grid_dim, block_dim, s, p);
+    const int bc = key_tile(D);
+    if (D == 64) {
+      if (bc == 32) launch<64, 32>(causal, grid_dim, block_dim, s, p);
+      else launch<64, 64>(causal, grid_dim, block_dim, s, p);
+    } else {
+      if (bc == 32) launch<128, 32>(causal, grid_dim, block_dim, s, p);
+      else launch<128, 64>(causal, grid_dim, block_dim, s, p);
+    }
   }
   if (hipGetLastError() != hipSuccess) return ATTN_FWD_ELAUNCH;
   return ATTN_FWD_OK;
