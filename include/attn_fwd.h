@@ -28,11 +28,14 @@ extern "C" {
 /* Return codes. */
 #define ATTN_FWD_OK            0   /* success: the kernel was enqueued on the stream        */
 #define ATTN_FWD_EINVAL       -1   /* NULL pointer; B, H or N < 1; causal not 0/1; scale not
-                                      finite or <= 0; sizes whose element counts overflow
-                                      (N*D >= 2^31 or B*H*N >= 2^40)                         */
+                                      finite or <= 0; sizes that overflow the kernel's
+                                      indexing (N*D >= 2^31, or B*H*ceil(N/128) >= 2^31
+                                      workgroups)                                           */
 #define ATTN_FWD_EUNSUPPORTED -2   /* head dimension D other than 64 or 128                  */
 #define ATTN_FWD_EALIGN       -3   /* q, k, v or o not 16-byte aligned, or lse not 4-byte    */
-#define ATTN_FWD_ELAUNCH      -4   /* the HIP runtime reported an error for the launch       */
+#define ATTN_FWD_ELAUNCH      -4   /* hipGetLastError() was set after the launch (this also
+                                      reports, and clears, an error left pending by an
+                                      earlier HIP call on the calling thread)                 */
 
 /*
  * attn_fwd - enqueue the attention forward of all B*H heads on one HIP stream.
@@ -50,8 +53,9 @@ extern "C" {
  *   stream   a hipStream_t passed as void*; NULL is the default stream.
  *
  * Ownership: the caller owns every buffer. The library allocates no device memory, keeps
- * no state between calls apart from a per-process cache of the device's compute-unit
- * count, and may be called concurrently from several host threads on different streams.
+ * no state between calls (apart from reading the tuning variable ATTN_FWD_BC once per
+ * process: 32 or 64 keys per tile, default 64), and may be called concurrently from
+ * several host threads on different streams.
  *
  * Behaviour: arguments are validated on the host before any HIP call; an invalid call
  * returns a negative code and enqueues nothing. A valid call enqueues one kernel and

@@ -10,7 +10,8 @@
 // those pages; they follow the usual FlashAttention conventions.
 //
 // gfx950 design (not the H100 one):
-//   * one workgroup = 4 waves; each wave owns 32 query rows, so a workgroup covers 128.
+//   * one workgroup = 4 waves; each wave owns 32 query rows, so a workgroup covers 128;
+//     two workgroups share a compute unit (two waves per SIMD).
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: lane l
 //     then holds 16 keys of query (l % 32) per 32-key block, so the row max and row sum
 //     are in-lane reductions plus one v_permlane32_swap between the two lane halves.
@@ -18,11 +19,14 @@
 //     are already the B operand of that MFMA (8 keys of its query), given that the A
 //     operand (V^T) pairs its k positions with the same 8 keys; V^T fragments come from
 //     LDS through ds_read_b64_tr_b16, which transposes 4x16 bf16 blocks across lanes.
-//   * K and V tiles (64 keys each) are staged through registers into a double-buffered
-//     LDS ring whose 16-byte chunks are XOR-swizzled by row, so the row-wise K reads and
-//     the transposing V reads spread over the LDS banks.
+//   * K and V tiles (64 keys by default, or 32) are copied global -> LDS by
+//     buffer_load ... lds into double-buffered rings; the K ring runs one tile ahead, so
+//     the score MFMAs of tile t+1 overlap the exponentials of tile t. The 16-byte chunks of
+//     each tile row are permuted so that the K reads and the transposing V reads are free
+//     of LDS bank conflicts.
 //   * the exp2 argument is fma(s, c, -m*c) with c = scale*log2(e) in fp32, on the fp32
-//     accumulator (the scale is never folded into bf16 Q).
+//     accumulator (the scale is never folded into bf16 Q). The running max only moves
+//     when a row's max grows by more than 2^8 (lazy rescaling), so O is rarely rescaled.
 //   * blockIdx is remapped so that consecutive query tiles of one head land on the same
 //     XCD (workgroups are dealt round-robin over the 8 XCDs), keeping that head's K/V in
 //     one L2; causal launches take the longest query tiles first.
@@ -46,7 +50,6 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kQW = 32;              // query rows per wave
 constexpr int kBr = kWaves * kQW;    // query rows per workgroup
 constexpr float kLn2 = 0.693147180559945309f;
@@ -104,15 +107,15 @@ __device__ inline int swz_v(int r) {
   return ((r >> 1) & 1) << 2;
 }
 
-template <int D, int BC>
+template <int D, int BC, int W = kWaves>
 struct TileLayout {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kChunks = D / 8;                    // 16-byte chunks per row
   static constexpr int kTileBytes = BC * kRowBytes;        // one K or V tile
   static constexpr int kRowsPerCopy = 1024 / kRowBytes;    // rows one wave-wide copy fills
-  static constexpr int kCopies = kTileBytes / 1024 / kWaves;  // copies per wave per tile
+  static constexpr int kCopies = kTileBytes / 1024 / W;    // copies per wave per tile
   static constexpr int kLdsBytes = 4 * kTileBytes;         // K[2], V[2]
-  static_assert(kCopies * 1024 * kWaves == kTileBytes, "tile must split into 1 KiB copies per wave");
+  static_assert(kCopies * 1024 * W == kTileBytes, "tile must split into 1 KiB copies per wave");
   static_assert(kChunks >= 8, "the chunk permutations need 8 chunks per row");
   // copies whose lane offsets differ (the permutations repeat every 16 / 4 rows)
   static constexpr int kPeriodK = 16 / kRowsPerCopy < kCopies ? 16 / kRowsPerCopy : kCopies;
@@ -163,6 +166,8 @@ __device__ inline i32x4 make_rsrc(const void* base, uint32_t num_bytes) {
 // a ring slot that no wave reads until after the next barrier, and the reads of that
 // slot's previous contents all precede the barrier before the copy. M0 is used by
 // nothing else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved; see the comment above
 __device__ inline void copy16_to_lds(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %3\n\t"
@@ -172,6 +177,7 @@ __device__ inline void copy16_to_lds(i32x4 rsrc, uint32_t voff, uint32_t soff, u
       : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
       : "m0");
 }
+#pragma clang diagnostic pop
 
 __device__ inline void wait_copies_and_barrier() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -182,15 +188,16 @@ __device__ inline uint32_t lds_address(const char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-template <int D, int BC, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, int BC, int W, bool CAUSAL>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const Params p) {
   static_assert(D == 64 || D == 128, "head dimension");
   static_assert(BC == 32 || BC == 64, "key tile");
   constexpr int kBc = BC;
   constexpr int NB = BC / 32;  // 32-key score blocks per tile
-  using L = TileLayout<D, BC>;
+  using L = TileLayout<D, BC, W>;
   constexpr int RB = L::kRowBytes;
+  constexpr int kBrW = W * kQW;  // query rows per workgroup
   __shared__ __attribute__((aligned(1024))) char smem[L::kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -213,18 +220,18 @@ void attn_fwd_kernel(const Params p) {
   const size_t head = (size_t)bh * (size_t)N * D;
   const __bf16* Qh = p.q + head;
 
-  const int q0 = qt * kBr + wave * kQW;  // first query row of this wave
+  const int q0 = qt * kBrW + wave * kQW;  // first query row of this wave
   const int qrow = q0 + col;
   const bool wave_active = q0 < N;
 
   // ---- key range: the workgroup streams tiles up to its last query (causal) or N;
   // each wave computes only the tiles that hold keys visible to its rows.
-  const int wg_kv_end = CAUSAL ? min(N, (qt + 1) * kBr) : N;
+  const int wg_kv_end = CAUSAL ? min(N, (qt + 1) * kBrW) : N;
   const int ntiles = (wg_kv_end + kBc - 1) / kBc;
   const int wave_tiles = !wave_active ? 0 : CAUSAL ? (min(N, q0 + kQW) + kBc - 1) / kBc : ntiles;
 
-  // ---- K/V copies. Copy i of wave w fills tile rows (4w + i)*kRowsPerCopy + lane/kChunks
-  // (D = 128: 4 rows; D = 64: 8 rows), lane l writing physical chunk l % kChunks, so it
+  // ---- K/V copies. Copy i of wave w fills tile rows (w*kCopies + i)*kRowsPerCopy +
+  // lane/kChunks (kRowsPerCopy = 4 for D = 128, 8 for D = 64), lane l writing physical chunk l % kChunks, so it
   // fetches the logical chunk stored there. The per-lane source offsets inside a tile are
   // fixed; the tile start is the scalar offset. In a ragged last tile, rows at or past N
   // repeat key N-1 (finite data that receives probability 0), so no read leaves the tensor.
@@ -308,7 +315,7 @@ void attn_fwd_kernel(const Params p) {
     v_addr[d] = row * RB + 16 * (chunk ^ swz_v<D>(row)) + 8 * (jj & 1);
   }
 
-  // S^T (two 32-key x 32-query blocks) of the K tile at LDS offset kb
+  // S^T (NB blocks of 32 keys x 32 queries) of the K tile at LDS offset kb
   auto qk = [&](int kb, f32x16 (&s)[NB]) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -329,8 +336,9 @@ void attn_fwd_kernel(const Params p) {
   for (int d = 0; d < D / 32; ++d) o[d] = f32x16{};
 
   // Masking of tile t: keys past N and, causal, keys after the query. Only a wave's last
-  // tile can need it: a wave's rows span 32 queries and tiles 64 keys, so every earlier
-  // tile ends before the wave's first query, and only the last tile can pass N.
+  // tile can need it: a wave's rows span 32 queries and tiles 32 or 64 keys (aligned), so
+  // every earlier tile ends before the wave's first query, and only the last tile can
+  // pass N.
   auto mask_tile = [&](f32x16 (&s)[NB], int t) {
     const int key0 = t * kBc;
     if ((key0 + kBc > N) || (CAUSAL && key0 + kBc - 1 > q0)) {
@@ -468,363 +476,11 @@ void attn_fwd_kernel(const Params p) {
   }
 }
 
-// ---------------------------------------------------------------------------------------
-// Wide variant: one wave per SIMD, 64 query rows per wave as two independent 32-row blocks
-// (A and B), three-stage K/V rings (tiles of 32 keys for D = 128, 64 for D = 64). Every K or V fragment read from LDS feeds
-// one MFMA of each block, and while one block works through its exponentials the other
-// block's MFMAs keep the matrix core busy, so the VALU and MFMA work of a single wave
-// overlap. Up to 512 registers per wave (VGPR + AGPR).
-constexpr int kWideQW = 64;                 // query rows per wave (two 32-row blocks)
-constexpr int kWideBr = kWaves * kWideQW;   // 256 query rows per workgroup
-constexpr int kWideStages = 3;
-template <int D>
-constexpr int wide_bc() { return D == 128 ? 32 : 64; }  // keys per tile
-
-template <int D, int BC>
-__device__ inline void wide_schedule() {
-  // phase 1: (BC/32) x (D/16) score MFMA pairs (one K read each) || exponentials of both
-  // blocks (about 112 VALU instructions per block per 64 keys); reads two pairs ahead
-  constexpr int kQkReads = (BC / 32) * (D / 16);
-  constexpr int kValu = 112 * 2 * BC / 64;
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-  for (int i = 0; i < kQkReads; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                // MFMA (A, B)
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // next DS read (K)
-    __builtin_amdgcn_sched_group_barrier(0x002, kValu / kQkReads, 0);  // VALU
-  }
-  // phase 2: P V MFMA pairs, their transposing reads two pairs ahead
-  constexpr int kPvReads = (BC / 16) * (D / 32);
-#pragma unroll
-  for (int i = 0; i < kPvReads; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA (A, B)
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (V^T)
-    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
-  }
-}
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_fwd_wide_kernel(const Params p) {
-  static_assert(D == 64 || D == 128, "head dimension");
-  constexpr int BC = wide_bc<D>();
-  constexpr int NB = BC / 32;  // 32-key score blocks per tile
-  constexpr int QB = 2;        // 32-row query blocks per wave
-  using L = TileLayout<D, BC>;
-  constexpr int RB = L::kRowBytes;
-  constexpr int T = L::kTileBytes;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kWideStages * T];  // K[3], V[3]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31;
-  const int hi = lane >> 5;
-
-  // ---- work unit
-  int g = blockIdx.x;
-  if (p.remap) {
-    const int per_xcd = gridDim.x >> 3;
-    g = (g & 7) * per_xcd + (g >> 3);
-  }
-  const int bh = g / p.n_qtiles;
-  int qt = g - bh * p.n_qtiles;
-  if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // longest tiles first
-  const int N = p.N;
-  const float c = p.c;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const __bf16* Qh = p.q + head;
-
-  const int q0 = qt * kWideBr + wave * kWideQW;  // first query row of this wave
-  const bool wave_active = q0 < N;
-  const int wg_kv_end = CAUSAL ? min(N, (qt + 1) * kWideBr) : N;
-  const int ntiles = (wg_kv_end + BC - 1) / BC;
-  const int wave_tiles = !wave_active ? 0 : CAUSAL ? (min(N, q0 + kWideQW) + BC - 1) / BC : ntiles;
-
-  // ---- K/V copies (same scheme as the narrow kernel; runtime ring slot in M0)
-  const uint32_t head_bytes = (uint32_t)N * RB;
-  const i32x4 krsrc = make_rsrc(p.k + head, head_bytes);
-  const i32x4 vrsrc = make_rsrc(p.v + head, head_bytes);
-  uint32_t koff[L::kPeriodK], voff[L::kPeriodV];
-#pragma unroll
-  for (int i = 0; i < L::kPeriodK; ++i) {
-    const int row = (wave * L::kCopies + i) * L::kRowsPerCopy + lane / L::kChunks;
-    koff[i] = row * RB + (((lane % L::kChunks) ^ swz_k<D>(row)) << 4);
-  }
-#pragma unroll
-  for (int i = 0; i < L::kPeriodV; ++i) {
-    const int row = (wave * L::kCopies + i) * L::kRowsPerCopy + lane / L::kChunks;
-    voff[i] = row * RB + (((lane % L::kChunks) ^ swz_v<D>(row)) << 4);
-  }
-  const uint32_t smem_lds = lds_address(smem);
-  auto copy_tile = [&](const i32x4& rsrc, const uint32_t* coff, int period, int t, uint32_t dst) {
-    const int key0 = t * BC;
-    const uint32_t dst_w = dst + wave * L::kCopies * 1024;
-    if (key0 + BC <= N) {
-#pragma unroll
-      for (int i = 0; i < L::kCopies; ++i) {
-        const uint32_t soff = __builtin_amdgcn_readfirstlane(key0 * RB + (i / period) * period * 1024);
-        copy16_to_lds(rsrc, coff[i % period], soff, dst_w + i * 1024);
-      }
-    } else {
-      const uint32_t last = (uint32_t)(N - key0 - 1);
-      const uint32_t soff = __builtin_amdgcn_readfirstlane(key0 * RB);
-#pragma unroll
-      for (int i = 0; i < L::kCopies; ++i) {
-        const uint32_t o = coff[i % period] + (i / period) * period * 1024;
-        copy16_to_lds(rsrc, (min(o / RB, last) * RB) | (o % RB), soff, dst_w + i * 1024);
-      }
-    }
-  };
-  auto copy_k = [&](int t) { copy_tile(krsrc, koff, L::kPeriodK, t, smem_lds + (t % kWideStages) * T); };
-  auto copy_v = [&](int t) {
-    copy_tile(vrsrc, voff, L::kPeriodV, t, smem_lds + (kWideStages + t % kWideStages) * T);
-  };
-  // Wait for every copy except the `in_flight` most recent ones, then barrier.
-  auto wait_and_barrier = [&](int in_flight) {
-    if (in_flight == 2 * L::kCopies) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L::kCopies) : "memory");
-    else if (in_flight == L::kCopies) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L::kCopies) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  };
-
-  copy_k(0);
-  if (ntiles > 1) copy_k(1);
-  copy_v(0);
-
-  // ---- Q fragments of both blocks
-  bf16x8 qf[QB][D / 16];
-#pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    const int qrow = q0 + 32 * b + col;
-    if (qrow < N) {
-      const bf16x8* src = reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D) + hi;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) qf[b][s] = src[2 * s];
-    } else {
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) qf[b][s] = bf16x8{};
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // see the narrow kernel
-
-  // ---- per-lane LDS read bases (as in the narrow kernel)
-  int k_addr[D / 16];
-#pragma unroll
-  for (int st = 0; st < D / 16; ++st) k_addr[st] = col * RB + 16 * ((2 * st + hi) ^ swz_k<D>(col));
-  const int jj = lane & 15;
-  const int grp = lane >> 4;
-  int v_addr[D / 32];
-#pragma unroll
-  for (int d = 0; d < D / 32; ++d) {
-    const int row = 4 * hi + (jj >> 2);
-    const int chunk = 4 * d + 2 * (grp & 1) + ((jj >> 1) & 1);
-    v_addr[d] = row * RB + 16 * (chunk ^ swz_v<D>(row)) + 8 * (jj & 1);
-  }
-
-  // scores of both blocks for the K tile in ring slot ks (a constant in the unrolled main
-  // loop, so the slot offset folds into the read's immediate)
-  auto qk = [&](int ks, f32x16 (&s)[QB][NB]) {
-    const char* kb = smem + ks * T;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      s[0][j] = f32x16{};
-      s[1][j] = f32x16{};
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + k_addr[st] + 32 * j * RB);
-        s[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][st], s[0][j], 0, 0, 0);
-        s[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[1][st], s[1][j], 0, 0, 0);
-      }
-    }
-  };
-
-  float m[QB] = {-INFINITY, -INFINITY};
-  float l[QB] = {0.f, 0.f};
-  f32x16 o[QB][D / 32];
-#pragma unroll
-  for (int b = 0; b < QB; ++b)
-#pragma unroll
-    for (int d = 0; d < D / 32; ++d) o[b][d] = f32x16{};
-
-  auto mask_tile = [&](f32x16 (&s)[QB][NB], int t) {
-    const int key0 = t * BC;
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      const int qb0 = q0 + 32 * b;
-      if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qb0)) {
-        const int limit = (CAUSAL ? min(N, qb0 + col + 1) : N) - key0 - 4 * hi;
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * j + 8 * (r >> 2) + (r & 3) >= limit) s[b][j][r] = -INFINITY;
-      }
-    }
-  };
-  auto softmax_head = [&](f32x16 (&s)[QB][NB]) {
-    float mx[QB];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      mx[b] = m[b];
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx[b] = fmaxf(mx[b], s[b][j][r]);
-      mx[b] = max_across_halves(mx[b]);
-    }
-    // lazy rescale (see the narrow kernel); one decision for both blocks
-    if (__builtin_amdgcn_ballot_w64((mx[0] - m[0]) * c > kRescaleLog2 || (mx[1] - m[1]) * c > kRescaleLog2)) {
-#pragma unroll
-      for (int b = 0; b < QB; ++b) {
-        const float alpha = __builtin_amdgcn_exp2f((m[b] - mx[b]) * c);
-        m[b] = mx[b];
-        l[b] *= alpha;
-#pragma unroll
-        for (int d = 0; d < D / 32; ++d)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[b][d][r] *= alpha;
-      }
-    }
-  };
-  auto exp_pv = [&](int vs, const f32x16 (&s)[QB][NB]) {
-    const char* vb = smem + (kWideStages + vs) * T;
-    bf16x8 pb[QB][2 * NB];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      const float mc = m[b] * c;
-      float rs = 0.f;
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][j][r], c, -mc));
-          rs += e;
-          pb[b][2 * j + (r >> 3)][r & 7] = (__bf16)e;
-        }
-      l[b] += rs;
-    }
-#pragma unroll
-    for (int st = 0; st < BC / 16; ++st) {
-#pragma unroll
-      for (int d = 0; d < D / 32; ++d) {
-        const char* a0 = vb + v_addr[d] + 16 * st * RB;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a0);
-        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
-        const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[0][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[0][st], o[0][d], 0, 0, 0);
-        o[1][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[1][st], o[1][d], 0, 0, 0);
-      }
-    }
-  };
-
-  // copies of iteration t: K(t+3) and V(t+2); returns how many this wave issued
-  auto copies = [&](int t) {
-    int n = 0;
-    if (t + 3 < ntiles) { copy_k(t + 3); n += L::kCopies; }
-    if (t + 2 < ntiles) { copy_v(t + 2); n += L::kCopies; }
-    return n;
-  };
-
-  // ---- prologue: K(0), K(1), V(0) in flight; scores of tile 0; then K(2), V(1)
-  f32x16 sa[QB][NB], sb[QB][NB];
-  wait_and_barrier((ntiles > 1 ? L::kCopies : 0) + L::kCopies);  // K(0) landed
-  if (wave_tiles > 0) qk(0, sa);
-  {
-    int n = 0;
-    if (ntiles > 2) { copy_k(2); n += L::kCopies; }
-    if (ntiles > 1) { copy_v(1); n += L::kCopies; }
-    wait_and_barrier(n);  // K(1), V(0) landed
-  }
-
-  // iteration t: scores of tile t in cur; K(t+1) is in ring slot (t+1) % 3, V(t) in t % 3
-  auto steady = [&](int kslot, int vslot, f32x16 (&cur)[QB][NB], f32x16 (&nxt)[QB][NB], int t) {
-    const int n = copies(t);
-    softmax_head(cur);
-    qk(kslot, nxt);
-    exp_pv(vslot, cur);
-    wide_schedule<D, BC>();
-    wait_and_barrier(n);
-  };
-  auto last = [&](int vslot, f32x16 (&cur)[QB][NB], int t) {
-    const int n = copies(t);
-    mask_tile(cur, t);
-    softmax_head(cur);
-    exp_pv(vslot, cur);
-    wait_and_barrier(n);
-  };
-
-  // Main loop: six steps per trip (lcm of the two score buffers and the three ring slots),
-  // all slots compile-time constants. A wave's rows span kMaskTiles tiles, so only its last
-  // kMaskTiles tiles can hold its diagonal (causal) or the ragged end; the main loop stops
-  // before them, and the remaining tiles go through one runtime-slot loop that masks and
-  // copies the scores back into sa, so no other code path holds them elsewhere.
-  constexpr int kMaskTiles = (kWideQW + BC - 1) / BC;
-  auto steady_masked = [&](int kslot, int vslot, f32x16 (&cur)[QB][NB], f32x16 (&nxt)[QB][NB], int t) {
-    const int n = copies(t);
-    mask_tile(cur, t);
-    softmax_head(cur);
-    qk(kslot, nxt);
-    exp_pv(vslot, cur);
-    wide_schedule<D, BC>();
-    wait_and_barrier(n);
-  };
-  int t = 0;
-  for (; t + 5 + kMaskTiles < wave_tiles; t += 6) {
-    steady(1, 0, sa, sb, t);
-    steady(2, 1, sb, sa, t + 1);
-    steady(0, 2, sa, sb, t + 2);
-    steady(1, 0, sb, sa, t + 3);
-    steady(2, 1, sa, sb, t + 4);
-    steady(0, 2, sb, sa, t + 5);
-  }
-  for (; t + 1 < wave_tiles; ++t) {
-    steady_masked((t + 1) % kWideStages, t % kWideStages, sa, sb, t);
-#pragma unroll
-    for (int b = 0; b < QB; ++b)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) sa[b][j] = sb[b][j];
-  }
-  if (t < wave_tiles) {
-    last(t % kWideStages, sa, t);
-    ++t;
-  }
-  for (; t < ntiles; ++t) wait_and_barrier(copies(t));
-
-  // ---- epilogue
-  if (wave_active) {
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      const float lt = sum_across_halves(l[b]);
-      const int qrow = q0 + 32 * b + col;
-      if (qrow < N) {
-        const float inv = 1.f / lt;
-        __bf16* orow = p.o + head + (size_t)qrow * D;
-#pragma unroll
-        for (int d = 0; d < D / 32; ++d)
-#pragma unroll
-          for (int j4 = 0; j4 < 4; ++j4) {
-            bf16x4 w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = (__bf16)(o[b][d][4 * j4 + i] * inv);
-            *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * j4 + 4 * hi) = w;
-          }
-        if (hi == 0) p.lse[(size_t)bh * N + qrow] = (m[b] * c + __builtin_log2f(lt)) * kLn2;
-      }
-    }
-  }
-}
-
-template <int D>
-void launch_wide(int causal, dim3 grid, dim3 block, hipStream_t s, const Params& p) {
-  if (causal) hipLaunchKernelGGL((attn_fwd_wide_kernel<D, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((attn_fwd_wide_kernel<D, false>), grid, block, 0, s, p);
-}
-
-template <int D, int BC>
-void launch(int causal, dim3 grid, dim3 block, hipStream_t s, const Params& p) {
-  if (causal) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, false>), grid, block, 0, s, p);
+template <int D, int BC, int W>
+void launch(int causal, dim3 grid, hipStream_t s, const Params& p) {
+  const dim3 block(64 * W);
+  if (causal) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, W, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, W, false>), grid, block, 0, s, p);
 }
 
 // Keys per K/V tile for head dimension D. ATTN_FWD_BC (32 or 64), read once, overrides
@@ -837,19 +493,6 @@ int key_tile(int D) {
   }();
   if (forced) return forced;
   return 64;
-}
-
-// Kernel family: "wide" (64 rows per wave, one wave per SIMD) or "narrow" (32 rows per
-// wave, two waves per SIMD). ATTN_FWD_KERNEL, read once, overrides the default for tuning.
-bool use_wide_kernel() {
-  static const int forced = [] {
-    const char* e = getenv("ATTN_FWD_KERNEL");
-    if (!e) return -1;
-    if (e[0] == 'w') return 1;
-    if (e[0] == 'n') return 0;
-    return -1;
-  }();
-  return forced == 1;
 }
 
 }  // namespace
@@ -874,9 +517,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (causal != 0 && causal != 1) return ATTN_FWD_EINVAL;
   if (!(scale > 0.f) || !isfinite(scale)) return ATTN_FWD_EINVAL;
   if (D != 64 && D != 128) return ATTN_FWD_EUNSUPPORTED;
-  const bool wide = use_wide_kernel();
-  const int br = wide ? kWideBr : kBr;
-  const int64_t n_qtiles = ((int64_t)N + br - 1) / br;
+  const int64_t n_qtiles = ((int64_t)N + kBr - 1) / kBr;
   const int64_t grid = (int64_t)B * H * n_qtiles;
   if ((int64_t)N * D >= ((int64_t)1 << 31) || grid >= ((int64_t)1 << 31)) return ATTN_FWD_EINVAL;
   const uintptr_t a16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o;
@@ -894,19 +535,14 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.c = scale * kLog2e;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid_dim((unsigned)grid), block_dim(kThreads);
-  if (wide) {
-    if (D == 64) launch_wide<64>(causal, grid_dim, block_dim, s, p);
-    else launch_wide<128>(causal, grid_dim, block_dim, s, p);
+  const dim3 grid_dim((unsigned)grid);
+  const int bc = key_tile(D);
+  if (D == 64) {
+    if (bc == 32) launch<64, 32, kWaves>(causal, grid_dim, s, p);
+    else launch<64, 64, kWaves>(causal, grid_dim, s, p);
   } else {
-    const int bc = key_tile(D);
-    if (D == 64) {
-      if (bc == 32) launch<64, 32>(causal, grid_dim, block_dim, s, p);
-      else launch<64, 64>(causal, grid_dim, block_dim, s, p);
-    } else {
-      if (bc == 32) launch<128, 32>(causal, grid_dim, block_dim, s, p);
-      else launch<128, 64>(causal, grid_dim, block_dim, s, p);
-    }
+    if (bc == 32) launch<128, 32, kWaves>(causal, grid_dim, s, p);
+    else launch<128, 64, kWaves>(causal, grid_dim, s, p);
   }
   if (hipGetLastError() != hipSuccess) return ATTN_FWD_ELAUNCH;
   return ATTN_FWD_OK;
