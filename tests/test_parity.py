@@ -11,6 +11,7 @@ check whole-tensor properties that hold at any size.
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -247,3 +248,43 @@ def test_workload_full_size_sampled(wid):
     og = o.cpu()[idx_b, idx_h, idx_i]
     lg = lse.cpu()[idx_b, idx_h, idx_i]
     check(og, lg, o_ref, lse_ref, f"{w.describe()} ({len(rows)} sampled rows)")
+
+
+@pytest.mark.parametrize("wid", [2, 3, 4, 5])
+def test_workload_full_size_every_element(wid):
+    """The benchmark's launch at full size, compared element by element over the whole
+    tensor with the fp64 oracle (run on the host cores, 16 heads at a time)."""
+    from threadpoolctl import threadpool_limits
+
+    w = WORKLOADS[wid]
+    print(f"[parity] generating {w.describe()}", flush=True)
+    q, k, v = workload_inputs(w)
+    dev = torch.device("cuda:0")
+    o, lse = attn_fwd(q.to(dev), k.to(dev), v.to(dev), causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    workers = min(16, len(os.sched_getaffinity(0)))
+    qf, kf, vf = (t.view(w.B * w.H, 1, w.N, w.D) for t in (q, k, v))
+    of, lf = o.view(w.B * w.H, w.N, w.D), lse.view(w.B * w.H, w.N)
+    max_abs = lse_err = 0.0
+    diff2 = ref2 = 0.0
+    worst = None
+    with threadpool_limits(limits=1):
+        for h0 in range(0, w.B * w.H, 16):
+            h1 = min(w.B * w.H, h0 + 16)
+            o_ref, lse_ref = oracle.attention_fwd(f64(qf[h0:h1]).swapaxes(0, 1), f64(kf[h0:h1]).swapaxes(0, 1),
+                                                  f64(vf[h0:h1]).swapaxes(0, 1), w.causal, w.scale,
+                                                  workers=workers)
+            d = f64(of[h0:h1]) - o_ref[0]
+            assert np.isfinite(d).all(), "non-finite output"
+            per_head = np.abs(d).reshape(h1 - h0, -1).max(axis=1)
+            if per_head.max() > max_abs:
+                max_abs = float(per_head.max())
+                worst = h0 + int(per_head.argmax())
+            diff2 += float((d * d).sum())
+            ref2 += float((o_ref * o_ref).sum())
+            lse_err = max(lse_err, float(np.abs(f64(lf[h0:h1]) - lse_ref[0]).max()))
+    rel = math.sqrt(diff2 / ref2)
+    print(f"[parity] {w.describe()} (all {w.B * w.H * w.N} rows): O max-abs {max_abs:.3e} "
+          f"(worst head {worst}) rel-L2 {rel:.3e} lse max-abs {lse_err:.3e}", flush=True)
+    assert max_abs <= O_MAX_ABS and rel <= O_REL_L2 and lse_err <= LSE_MAX_ABS
