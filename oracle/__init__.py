@@ -1,4 +1,4 @@
-"""CPU oracle for the fused softmax attention forward pass (fp64).
+"""CPU oracle for the fused softmax attention forward and backward passes (fp64).
 
 TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package. The product path (the HIP
@@ -8,11 +8,14 @@ code. Modules:
   attention  the plain definition in numpy float64 (full tensors, selected rows, P matrix)
   brute      pure-Python loops with math.fsum, for tiny shapes
   online     the pages' tiled online-softmax recurrence in float64 (to pin the identity)
+  backward   the gradients dQ, dK, dV of the forward definition, by the chain rule
 
-Every function here is pinned by ``tests/test_oracle.py`` against closed forms,
-invariants, a hand-derived worked example and brute force.
+Every function here is pinned by ``tests/test_oracle.py`` and ``tests/test_oracle_bwd.py``
+against closed forms, invariants, a hand-derived worked example, brute force and finite
+differences.
 """
 from .attention import attention_fwd, attention_head, attention_probs, attention_rows
+from .backward import attention_bwd, attention_bwd_head
 from .brute import attention_brute
 from .online import attention_online
 
@@ -23,4 +26,6 @@ __all__ = [
     "attention_rows",
     "attention_brute",
     "attention_online",
+    "attention_bwd",
+    "attention_bwd_head",
 ]
