@@ -1,8 +1,10 @@
-"""MI355X-native fused softmax attention forward (gfx950 HIP kernels behind a C ABI).
+"""MI355X-native fused softmax attention (gfx950 HIP kernels behind a C ABI).
 
-``attn_fwd`` is the thin Python binding over ``libattn_fwd.so``; the library is loaded
-on first use and its absence is an error (there is no fallback path).
+``attn_fwd`` and ``attn_bwd`` are thin Python bindings over ``libattn_fwd.so``; the
+library is loaded on first use and its absence is an error (there is no fallback path).
 """
-from .binding import attn_fwd, library_path, load_library, AttnFwdError
+from .binding import (AttnBwdError, AttnFwdError, attn_bwd, attn_fwd, bwd_workspace_bytes,
+                      library_path, load_library)
 
-__all__ = ["attn_fwd", "library_path", "load_library", "AttnFwdError"]
+__all__ = ["attn_fwd", "attn_bwd", "bwd_workspace_bytes", "library_path", "load_library",
+           "AttnFwdError", "AttnBwdError"]

@@ -1,4 +1,4 @@
-"""Python binding of the C-ABI attention forward library (``libattn_fwd.so``).
+"""Python binding of the C-ABI attention library (``libattn_fwd.so``).
 
 Argument marshalling only: shapes, dtypes and devices are checked, output tensors are
 allocated with torch when the caller gives none, and the C entry point is called with raw
@@ -6,9 +6,13 @@ device pointers and the current HIP stream. Every step of the computation runs i
 library's HIP kernels; if the library is missing this module raises instead of computing
 anything itself.
 
-C entry points (declared in include/attn_fwd.h):
+C entry points (declared in include/attn_fwd.h and include/attn_bwd.h):
   int attn_fwd(q, k, v, o, lse, B, H, N, D, causal, scale, stream)
   const char* attn_fwd_strerror(int code)
+  size_t attn_bwd_workspace_bytes(B, H, N)
+  int attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
+               B, H, N, D, causal, scale, stream)
+  const char* attn_bwd_strerror(int code)
 """
 from __future__ import annotations
 
@@ -26,6 +30,7 @@ ATTN_FWD_EINVAL = -1
 ATTN_FWD_EUNSUPPORTED = -2
 ATTN_FWD_EALIGN = -3
 ATTN_FWD_ELAUNCH = -4
+ATTN_BWD_EWORKSPACE = -5
 
 _lock = threading.Lock()
 _lib = None
@@ -61,6 +66,13 @@ def load_library():
         lib.attn_fwd.restype = ci
         lib.attn_fwd_strerror.argtypes = [ci]
         lib.attn_fwd_strerror.restype = ctypes.c_char_p
+        sz = ctypes.c_size_t
+        lib.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci]
+        lib.attn_bwd_workspace_bytes.restype = sz
+        lib.attn_bwd.argtypes = [vp] * 10 + [sz] + [ci] * 5 + [ctypes.c_float, vp]
+        lib.attn_bwd.restype = ci
+        lib.attn_bwd_strerror.argtypes = [ci]
+        lib.attn_bwd_strerror.restype = ctypes.c_char_p
         _lib = lib
         return lib
 
@@ -72,6 +84,28 @@ def strerror(code: int) -> str:
 def _current_stream_handle(device) -> int:
     import torch
     return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _stream_handle(stream, device) -> int:
+    if stream is None:
+        return _current_stream_handle(device)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _check_bf16(name, t):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must have shape [B, H, N, D]")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
 
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
@@ -88,16 +122,7 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor):
-            raise TypeError(f"{name} must be a torch.Tensor")
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
-        if t.dim() != 4:
-            raise ValueError(f"{name} must have shape [B, H, N, D]")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
+        _check_bf16(name, t)
     if not (q.shape == k.shape == v.shape):
         raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
     if not (q.device == k.device == v.device):
@@ -113,12 +138,7 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     elif (tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()
           or lse.device != q.device):
         raise ValueError("lse must be a contiguous float32 tensor of shape [B, H, N] on q's device")
-    if stream is None:
-        handle = _current_stream_handle(q.device)
-    elif isinstance(stream, int):
-        handle = stream
-    else:
-        handle = int(stream.cuda_stream)
+    handle = _stream_handle(stream, q.device)
     lib = load_library()
     code = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                         B, H, N, D, int(bool(causal)), float(scale), handle)
@@ -128,3 +148,68 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
             raise ValueError(f"attn_fwd rejected its arguments (code {code}): {msg}")
         raise AttnFwdError(code, msg)
     return out, lse
+
+
+class AttnBwdError(RuntimeError):
+    """A nonzero return code from attn_bwd."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"attn_bwd failed with code {code}: {message}")
+        self.code = code
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(int(B), int(H), int(N)))
+
+
+def attn_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Attention backward on the GPU: returns (dQ, dK, dV), bfloat16 [B, H, N, D].
+
+    q, k, v, o, dout: contiguous bfloat16 CUDA tensors [B, H, N, D] (o and lse from
+    attn_fwd with the same causal and scale); lse: float32 [B, H, N]. dq/dk/dv may be
+    given to write in place; ``workspace`` (a uint8 CUDA tensor of at least
+    bwd_workspace_bytes(B, H, N) bytes, 256-byte aligned) is allocated when not given.
+    Asynchronous on ``stream`` (default: torch's current stream).
+    """
+    import torch
+
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_bf16(name, t)
+    if not (q.shape == k.shape == v.shape == o.shape == dout.shape):
+        raise ValueError("q, k, v, o, dout must have one shape")
+    if len({t.device for t in (q, k, v, o, dout)}) != 1:
+        raise ValueError("all tensors must be on the same device")
+    B, H, N, D = (int(x) for x in q.shape)
+    if (not isinstance(lse, torch.Tensor) or tuple(lse.shape) != (B, H, N)
+            or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, H, N] on q's device")
+    outs = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        else:
+            _check_bf16(name, t)
+            if t.shape != q.shape or t.device != q.device:
+                raise ValueError(f"{name} must be shaped like q on q's device")
+        outs.append(t)
+    lib = load_library()
+    need = int(lib.attn_bwd_workspace_bytes(B, H, N))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif (workspace.dtype != torch.uint8 or workspace.device != q.device
+          or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+    handle = _stream_handle(stream, q.device)
+    code = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                        lse.data_ptr(), outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(),
+                        workspace.data_ptr(), workspace.numel(), B, H, N, D, int(bool(causal)),
+                        float(scale), handle)
+    if code != ATTN_FWD_OK:
+        msg = lib.attn_bwd_strerror(code).decode()
+        if code in (ATTN_FWD_EINVAL, ATTN_FWD_EUNSUPPORTED, ATTN_FWD_EALIGN, ATTN_BWD_EWORKSPACE):
+            raise ValueError(f"attn_bwd rejected its arguments (code {code}): {msg}")
+        raise AttnBwdError(code, msg)
+    return tuple(outs)

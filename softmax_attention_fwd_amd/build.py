@@ -2,9 +2,10 @@
 
     python -m softmax_attention_fwd_amd.build        # or __graft_entry__.build()
 
-The library is one translation unit (csrc/attn_fwd.hip: kernels + C ABI). It is built
-for gfx950 only, with packed fp32 VALU instructions disabled (the compiler would
-otherwise form v_pk_* fp32 ops from plain float code).
+The library holds two translation units, each with its kernels and C entry points:
+csrc/attn_fwd.hip (the forward) and csrc/attn_bwd.hip (the backward). It is built for
+gfx950 only, with packed fp32 VALU instructions disabled (the compiler would otherwise
+form v_pk_* fp32 ops from plain float code).
 """
 from __future__ import annotations
 
@@ -15,7 +16,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "attn_fwd.hip")
+SRCS = [os.path.join(HERE, "csrc", "attn_fwd.hip"), os.path.join(HERE, "csrc", "attn_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libattn_fwd.so")
 ARCH = "gfx950"
@@ -41,7 +42,7 @@ def hipcc() -> str:
 def build(verbose: bool = False, extra_flags=()) -> str:
     """Compile the library (always, even if a build exists) and return its path."""
     tmp = OUT + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

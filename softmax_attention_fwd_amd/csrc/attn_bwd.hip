@@ -1,0 +1,470 @@
+// Attention backward for gfx950 (AMD Instinct MI355X, CDNA4): dQ, dK, dV of
+// O = softmax(scale * Q K^T [+ causal mask]) V from the forward's per-row lse.
+//
+// The pages list the attention backward among the tile library's kernels (the summary of
+// the ThunderKittens paper on groovesquid.com) without formulas. This is the gradient of
+// the forward definition by the chain rule, with the probabilities recomputed from the
+// scores and lse (so no N x N matrix is stored):
+//   P = exp(scale * Q K^T - lse),  dV = P^T dO,  dP = dO V^T,
+//   Delta_i = sum_d dO_id O_id (= sum_j P_ij dP_ij),  dS = P o (dP - Delta),
+//   dQ = scale * dS K,  dK = scale * dS^T Q.
+//
+// Three kernels on the caller's stream:
+//   * delta: Delta_i and lse_i * log2(e) per row, into the caller's workspace.
+//   * dkdv: one workgroup per 128 keys (32 per wave). K and V stay in registers as MFMA
+//     operands; Q and dO stream through LDS in tiles of 64 queries. Per 32 queries and
+//     32 keys: S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_bf16, each lane then holds
+//     one key and 16 queries), P and dS in registers, and dV^T += dO^T P,
+//     dK^T += Q^T dS with dO^T / Q^T read transposed from LDS (ds_read_b64_tr_b16) and
+//     P / dS straight from the score registers as the B operand (the MFMA's k order only
+//     has to agree between its operands).
+//   * dq: one workgroup per 128 queries (32 per wave), the forward's shape. Q and dO stay
+//     in registers; K and V stream through LDS in tiles of 64 keys. Per 32 keys:
+//     S^T = K Q^T and dP^T = V dO^T (each lane one query, 16 keys), dS^T, and
+//     dQ^T += K^T dS^T with K^T read transposed.
+// No atomics: every output element is owned by one wave. dQ, dK, dV are written in bf16
+// (round to nearest even) after scaling in fp32.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "attn_bwd.h"
+#include "tile_lds.h"
+
+namespace {
+
+using namespace attn_tile;
+
+constexpr int kWaves = 4;
+constexpr int kBlk = 32;            // keys (dkdv) or queries (dq) per wave
+constexpr int kWgRows = kWaves * kBlk;
+constexpr int kTile = 64;           // streamed rows per LDS tile
+
+struct BwdParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* o;
+  const __bf16* dout;
+  const float* lse;
+  float* delta;  // workspace: Delta per row
+  float* lse2;   // workspace: lse * log2(e) per row
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  int N;
+  int n_wg_tiles;  // ceil(N / kWgRows)
+  int rows;        // B * H * N
+  int remap;       // grid is a multiple of 8: XCD-aware order
+  float c;         // scale * log2(e)
+  float scale;
+};
+
+// ---- delta: Delta_i = sum_d dO_id O_id and lse_i * log2(e), one row per D/8 lanes.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const BwdParams p) {
+  constexpr int kLanesPerRow = D / 8;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int row = t / kLanesPerRow;
+  const int part = t % kLanesPerRow;
+  float acc = 0.f;
+  if (row < p.rows) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p.dout + (size_t)row * D + part * 8);
+    const bf16x8 b = *reinterpret_cast<const bf16x8*>(p.o + (size_t)row * D + part * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf((float)a[i], (float)b[i], acc);
+  }
+#pragma unroll
+  for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kLanesPerRow);
+  if (row < p.rows && part == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = p.lse[row] * kLog2e;
+  }
+}
+
+__device__ inline int remap_block(int g, int remap) {
+  if (!remap) return g;
+  const int per_xcd = gridDim.x >> 3;
+  return (g & 7) * per_xcd + (g >> 3);
+}
+
+// Row-read base of an MFMA A operand from a swz-permuted [rows, D] tile: lane (m + 32h)
+// reads logical chunk 2st + h of row m; the permutation depends on m only.
+template <int D>
+__device__ inline int row_read_addr(int col, int hi, int st) {
+  return col * (2 * D) + 16 * ((2 * st + hi) ^ swz<D>(col));
+}
+// Transposed-read base (ds_read_b64_tr_b16) of 4x16 blocks from a swz-permuted
+// [rows, D] tile, for output column block d and row half u: in each 16-lane group the
+// source lane jj supplies 8 bytes of row 8u + 4h + (jj >> 2) at logical column
+// 32d + 16(grp & 1) + 4(jj & 3); the instruction hands lane jj column jj of that 4-row
+// block. The permutation depends on the row mod 16, so row offsets that are multiples of
+// 16 are added as constants, while the two 8-row halves need bases of their own.
+template <int D>
+__device__ inline int tr_read_addr(int lane, int d, int u) {
+  const int jj = lane & 15, grp = lane >> 4, hi = lane >> 5;
+  const int row = 8 * u + 4 * hi + (jj >> 2);
+  const int chunk = 4 * d + 2 * (grp & 1) + ((jj >> 1) & 1);
+  return row * (2 * D) + 16 * (chunk ^ swz<D>(row)) + 8 * (jj & 1);
+}
+// A operand of MFMA k-step over rows row0..row0+15 (row0 a multiple of 16) for output
+// columns 32d.. from the tile at smem + tile: rows row0 + 4h + {0..3} (low four k) and
+// row0 + 8 + 4h + {0..3} (high four k), column 32d + lane % 32.
+template <int D>
+__device__ inline bf16x8 tr_frag(const char* smem, int tile, const int (&addr)[2], int row0) {
+  const char* base = smem + tile + row0 * (2 * D);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + addr[0]));
+  const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + addr[1]));
+  return __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Store a D x 32 fp32 accumulator (transposed layout: register r of block d holds column
+// 32d + 8(r/4) + 4h + r%4 of row `row`) as bf16 row `row` of out, times s.
+template <int D>
+__device__ inline void store_rows(__bf16* out_row, const f32x16 (&acc)[D / 32], int hi, float s) {
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+      bf16x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = (__bf16)(acc[d][4 * j4 + i] * s);
+      *reinterpret_cast<bf16x4*>(out_row + 32 * d + 8 * j4 + 4 * hi) = w;
+    }
+}
+
+// ---- dkdv: workgroup = 128 keys, wave = 32 keys; query tiles of 64 stream through LDS.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int RB = 2 * D;
+  constexpr int kTileBytes = kTile * RB;
+  constexpr int kSlot = 2 * kTileBytes + 2 * kTile * 4;  // Q, dO, lse2, Delta
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kSlot];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int hi = lane >> 5;
+  const int N = p.N;
+
+  const int g = remap_block(blockIdx.x, p.remap);
+  const int bh = g / p.n_wg_tiles;
+  const int kt = g - bh * p.n_wg_tiles;
+  const size_t head = (size_t)bh * N * D;
+  const int k0 = kt * kWgRows + wave * kBlk;  // first key of this wave
+  const int key = k0 + col;
+
+  // K and V as B operands (lane = key, k = D index 16st + 8h .. +7)
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const int r = min(key, N - 1);
+    const bf16x8* ks = reinterpret_cast<const bf16x8*>(p.k + head + (size_t)r * D) + hi;
+    const bf16x8* vs = reinterpret_cast<const bf16x8*>(p.v + head + (size_t)r * D) + hi;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      kf[s] = ks[2 * s];
+      vf[s] = vs[2 * s];
+    }
+  }
+  f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) {
+    dv[d] = f32x16{};
+    dk[d] = f32x16{};
+  }
+
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const i32x4 qrsrc = make_rsrc(p.q + head, head_bytes);
+  const i32x4 orsrc = make_rsrc(p.dout + head, head_bytes);
+  const i32x4 lrsrc = make_rsrc(p.lse2 + (size_t)bh * N, (uint32_t)N * 4u);
+  const i32x4 drsrc = make_rsrc(p.delta + (size_t)bh * N, (uint32_t)N * 4u);
+  const uint32_t smem_lds = lds_address(smem);
+
+  // query tiles: causal workgroups start at their first key
+  const int qt_first = CAUSAL ? (kt * kWgRows) / kTile : 0;
+  const int qt_end = (N + kTile - 1) / kTile;
+  auto load = [&](int qt, int slot) {
+    const uint32_t base = smem_lds + slot * kSlot;
+    copy_tile<D, kTile, kWaves>(qrsrc, qt * kTile, N, base, wave, lane);
+    copy_tile<D, kTile, kWaves>(orsrc, qt * kTile, N, base + kTileBytes, wave, lane);
+    if (wave == 0) copy_vec64(lrsrc, qt * kTile, N, base + 2 * kTileBytes, lane);
+    if (wave == 1) copy_vec64(drsrc, qt * kTile, N, base + 2 * kTileBytes + kTile * 4, lane);
+  };
+
+  int ra[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) ra[st] = row_read_addr<D>(col, hi, st);
+  int ta[D / 32][2];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) {
+    ta[d][0] = tr_read_addr<D>(lane, d, 0);
+    ta[d][1] = tr_read_addr<D>(lane, d, 1);
+  }
+
+  if (qt_first < qt_end) load(qt_first, 0);
+  for (int qt = qt_first; qt < qt_end; ++qt) {
+    const int slot = (qt - qt_first) & 1;
+    wait_copies_and_barrier();
+    if (qt + 1 < qt_end) load(qt + 1, slot ^ 1);
+    const int qs = slot * kSlot;                  // Q tile
+    const int os = qs + kTileBytes;               // dO tile
+    const int ls = qs + 2 * kTileBytes;           // lse2
+    const int ds = ls + kTile * 4;                // Delta
+#pragma unroll
+    for (int b = 0; b < kTile / kBlk; ++b) {
+      const int qb0 = qt * kTile + b * kBlk;  // first query of this block
+      if (CAUSAL && qb0 + kBlk - 1 < k0) continue;  // every query precedes every key
+      if (k0 >= N) continue;                        // wave past the last key
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(smem + qs + b * kBlk * RB + ra[st]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[st], s, 0, 0, 0);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(smem + os + b * kBlk * RB + ra[st]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[st], dp, 0, 0, 0);
+      }
+      // register r holds query qb0 + 8(r/4) + 4h + r%4 of key `key`
+      f32x4 l2[4], dl[4];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        l2[g4] = *reinterpret_cast<const f32x4*>(smem + ls + (b * kBlk + 8 * g4 + 4 * hi) * 4);
+        dl[g4] = *reinterpret_cast<const f32x4*>(smem + ds + (b * kBlk + 8 * g4 + 4 * hi) * 4);
+      }
+      const bool need_mask = (CAUSAL && qb0 < k0 + kBlk - 1) || (qb0 + kBlk > N);
+      // visible iff query < N and (causal) key <= query: query index minus this lane's
+      // offset 4h, against the limits
+      const int lo_lim = CAUSAL ? key - qb0 - 4 * hi : -1;  // need query offset >= lo_lim
+      const int hi_lim = N - qb0 - 4 * hi;                  // need query offset < hi_lim
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -l2[r >> 2][r & 3]));
+        if (need_mask) {
+          const int qo = 8 * (r >> 2) + (r & 3);
+          if (qo < lo_lim || qo >= hi_lim) pr = 0.f;
+        }
+        const float dsr = pr * (dp[r] - dl[r >> 2][r & 3]);
+        pb[r >> 3][r & 7] = (__bf16)pr;
+        sb[r >> 3][r & 7] = (__bf16)dsr;
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 queries (two k-steps of 16)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int d = 0; d < D / 32; ++d) {
+          const bf16x8 oa = tr_frag<D>(smem, os, ta[d], b * kBlk + 16 * st);
+          dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pb[st], dv[d], 0, 0, 0);
+          const bf16x8 qa = tr_frag<D>(smem, qs, ta[d], b * kBlk + 16 * st);
+          dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb[st], dk[d], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (key < N) {
+    store_rows<D>(p.dv + head + (size_t)key * D, dv, hi, 1.f);
+    store_rows<D>(p.dk + head + (size_t)key * D, dk, hi, p.scale);
+  }
+}
+
+// ---- dq: workgroup = 128 queries, wave = 32 queries; key tiles of 64 stream through LDS.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(const BwdParams p) {
+  constexpr int RB = 2 * D;
+  constexpr int kTileBytes = kTile * RB;
+  constexpr int kSlot = 2 * kTileBytes;  // K, V
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kSlot];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int hi = lane >> 5;
+  const int N = p.N;
+
+  const int g = remap_block(blockIdx.x, p.remap);
+  const int bh = g / p.n_wg_tiles;
+  int qt = g - bh * p.n_wg_tiles;
+  if (CAUSAL) qt = p.n_wg_tiles - 1 - qt;  // longest first
+  const size_t head = (size_t)bh * N * D;
+  const int q0 = qt * kWgRows + wave * kBlk;
+  const int qrow = q0 + col;
+
+  // Q and dO as B operands (lane = query, k = D index 16st + 8h .. +7)
+  bf16x8 qf[D / 16], of[D / 16];
+  float l2 = 0.f, dl = 0.f;
+  {
+    const int r = min(qrow, N - 1);
+    const bf16x8* qs = reinterpret_cast<const bf16x8*>(p.q + head + (size_t)r * D) + hi;
+    const bf16x8* os = reinterpret_cast<const bf16x8*>(p.dout + head + (size_t)r * D) + hi;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      qf[s] = qs[2 * s];
+      of[s] = os[2 * s];
+    }
+    l2 = p.lse2[(size_t)bh * N + r];
+    dl = p.delta[(size_t)bh * N + r];
+  }
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) dq[d] = f32x16{};
+
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const i32x4 krsrc = make_rsrc(p.k + head, head_bytes);
+  const i32x4 vrsrc = make_rsrc(p.v + head, head_bytes);
+  const uint32_t smem_lds = lds_address(smem);
+
+  const int wg_kv_end = CAUSAL ? min(N, (qt + 1) * kWgRows) : N;
+  const int nt = (wg_kv_end + kTile - 1) / kTile;
+  const int wave_kv_end = CAUSAL ? min(N, q0 + kBlk) : N;  // keys this wave needs
+  auto load = [&](int t, int slot) {
+    const uint32_t base = smem_lds + slot * kSlot;
+    copy_tile<D, kTile, kWaves>(krsrc, t * kTile, N, base, wave, lane);
+    copy_tile<D, kTile, kWaves>(vrsrc, t * kTile, N, base + kTileBytes, wave, lane);
+  };
+
+  int ra[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) ra[st] = row_read_addr<D>(col, hi, st);
+  int ta[D / 32][2];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) {
+    ta[d][0] = tr_read_addr<D>(lane, d, 0);
+    ta[d][1] = tr_read_addr<D>(lane, d, 1);
+  }
+
+  load(0, 0);
+  for (int t = 0; t < nt; ++t) {
+    const int slot = t & 1;
+    wait_copies_and_barrier();
+    if (t + 1 < nt) load(t + 1, slot ^ 1);
+    const int ks = slot * kSlot;
+    const int vs = ks + kTileBytes;
+#pragma unroll
+    for (int j = 0; j < kTile / kBlk; ++j) {
+      const int kb0 = t * kTile + j * kBlk;  // first key of this block
+      if (q0 >= N || kb0 >= wave_kv_end) continue;
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(smem + ks + j * kBlk * RB + ra[st]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s, 0, 0, 0);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(smem + vs + j * kBlk * RB + ra[st]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, of[st], dp, 0, 0, 0);
+      }
+      // register r holds key kb0 + 8(r/4) + 4h + r%4 of query qrow
+      const bool need_mask = (CAUSAL && kb0 + kBlk - 1 > q0) || (kb0 + kBlk > N);
+      const int lim = (CAUSAL ? min(N, qrow + 1) : N) - kb0 - 4 * hi;  // key offset < lim
+      bf16x8 sb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -l2));
+        if (need_mask && 8 * (r >> 2) + (r & 3) >= lim) pr = 0.f;
+        sb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - dl));
+      }
+      // dQ^T += K^T dS^T over the block's 32 keys
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int d = 0; d < D / 32; ++d) {
+          const bf16x8 ka = tr_frag<D>(smem, ks, ta[d], j * kBlk + 16 * st);
+          dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, sb[st], dq[d], 0, 0, 0);
+        }
+    }
+  }
+  if (qrow < N) store_rows<D>(p.dq + head + (size_t)qrow * D, dq, hi, p.scale);
+}
+
+template <int D>
+void launch_bwd(int causal, int B, int H, hipStream_t s, const BwdParams& p) {
+  const dim3 block(64 * kWaves);
+  const int rows_per_block = 256 / (D / 8);
+  hipLaunchKernelGGL(attn_bwd_delta_kernel<D>, dim3((p.rows + rows_per_block - 1) / rows_per_block),
+                     block, 0, s, p);
+  const dim3 grid((unsigned)(B * H * p.n_wg_tiles));
+  if (causal) {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), grid, block, 0, s, p);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), grid, block, 0, s, p);
+  }
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1) return 0;
+  return 2 * round_up((size_t)B * H * N * sizeof(float), 256);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int B, int H, int N, int D, int causal, float scale,
+             void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return ATTN_BWD_EINVAL;
+  if (B < 1 || H < 1 || N < 1) return ATTN_BWD_EINVAL;
+  if (causal != 0 && causal != 1) return ATTN_BWD_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_BWD_EINVAL;
+  if (D != 64 && D != 128) return ATTN_BWD_EUNSUPPORTED;
+  const int64_t n_tiles = ((int64_t)N + kWgRows - 1) / kWgRows;
+  const int64_t grid = (int64_t)B * H * n_tiles;
+  const int64_t rows = (int64_t)B * H * N;
+  if ((int64_t)N * D >= ((int64_t)1 << 31) || grid >= ((int64_t)1 << 31) ||
+      rows * (D / 8) >= ((int64_t)1 << 31))
+    return ATTN_BWD_EINVAL;
+  if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N)) return ATTN_BWD_EWORKSPACE;
+  const uintptr_t a16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o |
+                        (uintptr_t)dout | (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv;
+  if ((a16 & 15u) != 0 || ((uintptr_t)lse & 3u) != 0 || ((uintptr_t)workspace & 255u) != 0)
+    return ATTN_BWD_EALIGN;
+
+  BwdParams p;
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.o = static_cast<const __bf16*>(o);
+  p.dout = static_cast<const __bf16*>(dout);
+  p.lse = lse;
+  p.delta = static_cast<float*>(workspace);
+  p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    round_up((size_t)rows * sizeof(float), 256));
+  p.dq = static_cast<__bf16*>(dq);
+  p.dk = static_cast<__bf16*>(dk);
+  p.dv = static_cast<__bf16*>(dv);
+  p.N = N;
+  p.n_wg_tiles = (int)n_tiles;
+  p.rows = (int)rows;
+  p.remap = (grid % 8 == 0) ? 1 : 0;
+  p.c = scale * kLog2e;
+  p.scale = scale;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (D == 64) launch_bwd<64>(causal, B, H, s, p);
+  else launch_bwd<128>(causal, B, H, s, p);
+  if (hipGetLastError() != hipSuccess) return ATTN_BWD_ELAUNCH;
+  return ATTN_BWD_OK;
+}
+
+const char* attn_bwd_strerror(int code) {
+  switch (code) {
+    case ATTN_BWD_OK: return "success";
+    case ATTN_BWD_EINVAL: return "invalid argument (NULL pointer, size < 1, causal not 0/1, scale not finite and > 0, or size overflow)";
+    case ATTN_BWD_EUNSUPPORTED: return "unsupported head dimension (D must be 64 or 128)";
+    case ATTN_BWD_EALIGN: return "misaligned pointer (tensors need 16 bytes, lse 4, workspace 256)";
+    case ATTN_BWD_ELAUNCH: return "kernel launch failed";
+    case ATTN_BWD_EWORKSPACE: return "workspace smaller than attn_bwd_workspace_bytes(B, H, N)";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

@@ -8,7 +8,8 @@ Recipe (the pages fix none; the same recipe serves tests and the benchmark):
   one CPU ``torch.Generator`` per call, seeded with ``seed``; draw Q, then K, then V as
   float32 standard normals of shape [B, H, N, D]; multiply each by its sigma; round to
   bfloat16 with round-to-nearest-even (torch's float32 -> bfloat16 cast).
-The workloads use seed 1000 + workload number.
+The workloads use seed 1000 + workload number. The backward's incoming gradient dO is
+drawn the same way from its own generator (``make_dout``).
 """
 from __future__ import annotations
 
@@ -81,3 +82,15 @@ def make_qkv(B: int, H: int, N: int, D: int, seed: int, sigma_q: float = 1.0,
 def workload_inputs(w: Workload):
     """Q, K, V (CPU bfloat16) of a workload, from its own seed."""
     return make_qkv(w.B, w.H, w.N, w.D, w.seed, w.sigma_q, w.sigma_k, w.sigma_v)
+
+
+def make_dout(B: int, H: int, N: int, D: int, seed: int, sigma: float = 1.0):
+    """An incoming gradient dO for the backward pass: CPU bfloat16 [B, H, N, D] standard
+    normals times sigma, from a generator seeded with ``seed`` + 7919 (so it differs from
+    the Q, K, V of the same seed)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 7919)
+    x = torch.randn((B, H, N, D), generator=g, dtype=torch.float32)
+    if sigma != 1.0:
+        x.mul_(sigma)
+    return x.to(torch.bfloat16).contiguous()

@@ -15,6 +15,8 @@ import pytest
 from softmax_attention_fwd_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
 
 
@@ -26,24 +28,31 @@ def lib():
     return binding.load_library()
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(attn_fwd\w*)\s*\(", text, flags=re.M)))
+def declared_functions(path=None):
+    names = set()
+    for h in ([path] if path else HEADERS):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(attn_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
-def declared_codes():
-    text = open(HEADER).read()
-    return {name: int(val) for name, val in re.findall(r"#define\s+(ATTN_FWD_\w+)\s+(-?\d+)", text)}
+def declared_codes(prefix="ATTN_FWD_"):
+    text = "".join(open(h).read() for h in HEADERS)
+    return {name: int(val) for name, val in re.findall(r"#define\s+(" + prefix + r"\w+)\s+(-?\d+)", text)}
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_strerror"]
+    assert declared_functions() == ["attn_bwd", "attn_bwd_strerror", "attn_bwd_workspace_bytes",
+                                    "attn_fwd", "attn_fwd_strerror"]
 
 
 def test_exports_every_declared_symbol(lib):
+    import subprocess
+    exported = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
+                              capture_output=True, text=True, check=True).stdout.split()
     for name in declared_functions():
-        assert hasattr(lib, name), f"{name} declared in attn_fwd.h but not exported"
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+        assert name in exported
 
 
 def test_codes_match_binding():
@@ -55,6 +64,20 @@ def test_codes_match_binding():
         "ATTN_FWD_EALIGN": binding.ATTN_FWD_EALIGN,
         "ATTN_FWD_ELAUNCH": binding.ATTN_FWD_ELAUNCH,
     }
+
+
+def test_bwd_codes_match_binding():
+    assert declared_codes("ATTN_BWD_") == {
+        "ATTN_BWD_OK": 0, "ATTN_BWD_EINVAL": binding.ATTN_FWD_EINVAL,
+        "ATTN_BWD_EUNSUPPORTED": binding.ATTN_FWD_EUNSUPPORTED,
+        "ATTN_BWD_EALIGN": binding.ATTN_FWD_EALIGN, "ATTN_BWD_ELAUNCH": binding.ATTN_FWD_ELAUNCH,
+        "ATTN_BWD_EWORKSPACE": binding.ATTN_BWD_EWORKSPACE,
+    }
+
+
+def test_bwd_strerror(lib):
+    msgs = {lib.attn_bwd_strerror(c).decode() for c in declared_codes("ATTN_BWD_").values()}
+    assert len(msgs) == len(declared_codes("ATTN_BWD_")) and "unknown error code" not in msgs
 
 
 def test_strerror(lib):
@@ -110,3 +133,40 @@ def test_binding_missing_library_is_loud(monkeypatch, tmp_path):
     monkeypatch.setenv("ATTN_FWD_LIB", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         binding.load_library()
+
+
+def test_bwd_workspace_bytes(lib):
+    # two fp32 arrays of B*H*N, each rounded up to 256 bytes
+    assert lib.attn_bwd_workspace_bytes(2, 3, 100) == 2 * 2560
+    assert lib.attn_bwd_workspace_bytes(16, 16, 4096) == 2 * 16 * 16 * 4096 * 4
+    assert lib.attn_bwd_workspace_bytes(0, 1, 1) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 1, -3) == 0
+
+
+W = 0x100000  # 256-byte aligned fake workspace
+
+
+def call_bwd(lib, q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A, ws=W, ws_bytes=1 << 20,
+             B=1, H=1, N=128, D=64, causal=0, scale=0.125):
+    return lib.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, N, D, causal,
+                        ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(do=None), -1), (dict(lse=None), -1),
+    (dict(dq=None), -1), (dict(dv=None), -1), (dict(ws=None), -1),
+    (dict(B=0), -1), (dict(N=0), -1), (dict(causal=3), -1), (dict(scale=-2.0), -1),
+    (dict(scale=math.nan), -1), (dict(D=80), -2), (dict(N=1 << 24, D=128), -1),
+    (dict(ws_bytes=100), -5), (dict(B=16, H=16, N=4096, ws_bytes=1 << 20), -5),
+    (dict(do=A + 4), -3), (dict(dk=A + 2), -3), (dict(lse=A + 1), -3), (dict(ws=W + 16), -3),
+])
+def test_bwd_invalid_arguments_rejected(lib, kw, code):
+    assert call_bwd(lib, **kw) == code
+
+
+def test_bwd_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        binding.attn_bwd(q, q, q, q, q, lse)
