@@ -1,19 +1,22 @@
 #!/usr/bin/env python3
 """Attention forward throughput on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload 3] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload 3] [--gpus 1] [--op fwd|bwd]
 
 One step = one attn_fwd call (the whole fused forward: K/V streaming, both contractions,
-online softmax, epilogue) over the workload's full tensors, already resident in HBM.
+online softmax, epilogue) over the workload's full tensors, already resident in HBM; with
+--op bwd, one attn_bwd call (its three kernels: Delta, dK/dV, dQ) on the same shapes.
 The default workload is B16 H16 N4096 D128 non-causal with bf16 inputs. Prints ONE JSON
 line on stdout; details go to stderr.
 
 Reported:
-  value          whole-job TFLOP/s = 4*B*H*N^2*D (halved when causal) * K / (timed span)
-  roofline       the kernel's mean launch duration (HIP events on the launch stream)
+  value          whole-job TFLOP/s = F * K / (timed span), with F = 4*B*H*N^2*D for the
+                 forward and 10*B*H*N^2*D for the backward (its five N x N x D products),
+                 halved when causal
+  roofline       F over the mean duration of one call (HIP events on the launch stream)
                  against the bf16 dense MFMA peak
-  cpu_baseline   the fp64 numpy oracle, timed on this host's cores on a bounded sample
-                 of the same workload (a few heads), in the same unit
+  cpu_baseline   the fp64 numpy oracle of the same pass, timed on this host's cores on a
+                 bounded sample of the same workload (a few heads), in the same unit
 """
 from __future__ import annotations
 
@@ -63,8 +66,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, q, k, v, budget_s: float):
-    """Time the fp64 oracle on whole heads of the workload, one head per host core."""
+def cpu_baseline(w, q, k, v, budget_s: float, do=None):
+    """Time the fp64 oracle (forward, or backward when ``do`` is given) on whole heads of
+    the workload, one head per host core."""
     import numpy as np
 
     import oracle
@@ -73,13 +77,15 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     cores = len(os.sched_getaffinity(0))
-    per_head = w.flops / (w.B * w.H)
+    per_head = (w.flops if do is None else 2.5 * w.flops) / (w.B * w.H)
     heads = min(w.B * w.H, cores)
     b_idx = [i // w.H for i in range(heads)]
     h_idx = [i % w.H for i in range(heads)]
     qs = np.stack([q[b, h].double().numpy() for b, h in zip(b_idx, h_idx)])[None]
     ks = np.stack([k[b, h].double().numpy() for b, h in zip(b_idx, h_idx)])[None]
     vs = np.stack([v[b, h].double().numpy() for b, h in zip(b_idx, h_idx)])[None]
+    if do is not None:
+        dos = np.stack([do[b, h].double().numpy() for b, h in zip(b_idx, h_idx)])[None]
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     try:
         if ctx:
@@ -87,7 +93,10 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         done = 0
         t0 = time.perf_counter()
         while True:
-            oracle.attention_fwd(qs, ks, vs, w.causal, w.scale, workers=cores)
+            if do is None:
+                oracle.attention_fwd(qs, ks, vs, w.causal, w.scale, workers=cores)
+            else:
+                oracle.attention_bwd(qs, ks, vs, dos, w.causal, w.scale, workers=cores)
             done += heads
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -100,7 +109,8 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"{done} head-passes of {w.describe()} (first {heads} heads, "
+        "sample": (f"{done} head-passes ({'forward' if do is None else 'backward'}) of "
+                   f"{w.describe()} (first {heads} heads, "
                    f"{done * per_head:.3e} flop, fp64 numpy, one head per thread) in {dt:.1f} s"),
     }
 
@@ -112,6 +122,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=40,
                     help="untimed launches first; the shader clock settles over ~20 launches")
     ap.add_argument("--workload", type=int, default=3, help="1..5 (default 3)")
+    ap.add_argument("--op", choices=("fwd", "bwd"), default="fwd",
+                    help="the forward (default, the headline metric) or the backward pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -131,8 +143,8 @@ def main() -> int:
 
     import torch
 
-    from softmax_attention_fwd_amd import attn_fwd
-    from softmax_attention_fwd_amd.inputs import WORKLOADS, workload_inputs
+    from softmax_attention_fwd_amd import attn_bwd, attn_fwd, bwd_workspace_bytes
+    from softmax_attention_fwd_amd.inputs import WORKLOADS, make_dout, workload_inputs
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -145,8 +157,22 @@ def main() -> int:
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
+    flops = w.flops
+    do = None
+    if args.op == "fwd":
+        def step():
+            attn_fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+    else:
+        flops = 2.5 * w.flops
+        do = make_dout(w.B, w.H, w.N, w.D, seed=w.seed)
+        dod = do.to(dev)
         attn_fwd(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        grads = [torch.empty_like(qd) for _ in range(3)]
+        ws = torch.empty(bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+
+        def step():
+            attn_bwd(qd, kd, vd, o, dod, lse, causal=w.causal, scale=w.scale, dq=grads[0],
+                     dk=grads[1], dv=grads[2], workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -172,16 +198,19 @@ def main() -> int:
     launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     mean_launch = statistics.fmean(launch_ms)
     ms_per_step = total_ms / args.steps
-    value = w.flops * args.steps / (total_ms * 1e-3) / 1e12
-    achieved = w.flops / (mean_launch * 1e-3) / 1e12
+    value = flops * args.steps / (total_ms * 1e-3) / 1e12
+    achieved = flops / (mean_launch * 1e-3) / 1e12
     log(f"[bench] span {total_ms:.3f} ms for {args.steps} steps ({ms_per_step:.4f} ms/step, "
         f"wall {wall * 1e3:.1f} ms); launch median {statistics.median(launch_ms):.4f} "
         f"min {min(launch_ms):.4f} max {max(launch_ms):.4f} ms")
     log(f"[bench] {value:.1f} TFLOP/s whole-job; kernel {achieved:.1f} TFLOP/s = "
         f"{100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 dense peak")
 
+    metric = "attention fwd TFLOP/s and % of bf16 MFMA peak (B16 H16 N4096 D128)"
+    if args.op == "bwd":
+        metric = "attention bwd TFLOP/s (10*B*H*N^2*D, halved causal) and % of bf16 MFMA peak"
     result = {
-        "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak (B16 H16 N4096 D128)",
+        "metric": metric,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -193,7 +222,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 Q, K, V)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+        "config": {"workload": w.name, "op": args.op, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                    "causal": w.causal, "scale": w.scale, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "launch_ms": {"mean": round(mean_launch, 5), "median": round(statistics.median(launch_ms), 5),
@@ -204,8 +233,8 @@ def main() -> int:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(w.name),
-            "traffic_algorithmic": w.hbm_bytes,
+            "traffic": measured_traffic(w.name) if args.op == "fwd" else None,
+            "traffic_algorithmic": w.hbm_bytes if args.op == "fwd" else 16 * w.B * w.H * w.N * w.D + 12 * w.B * w.H * w.N,
         },
         "cpu_baseline": None,
     }
@@ -220,7 +249,7 @@ def main() -> int:
         del src, dst
     if not args.no_cpu_baseline:
         log(f"[bench] timing the fp64 oracle on host cores (~{args.cpu_seconds:.0f} s budget)")
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds, do=do)
         log(f"[bench] cpu baseline: {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
     return 0

@@ -10,7 +10,9 @@
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
 // Three kernels on the caller's stream:
-//   * delta: Delta_i and lse_i * log2(e) per row, into the caller's workspace.
+//   * delta: -Delta_i and -lse_i / scale per row, into the caller's workspace; they
+//     seed the dP and S accumulators, so the MFMAs produce dP - Delta and
+//     s - lse / scale directly (P = exp2(c (s - lse / scale)), c = scale * log2 e).
 //   * dkdv: one workgroup per 128 keys (32 per wave). K and V stay in registers as MFMA
 //     operands; Q and dO stream through LDS in tiles of 64 queries. Per 32 queries and
 //     32 keys: S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_bf16, each lane then holds
@@ -49,8 +51,8 @@ struct BwdParams {
   const __bf16* o;
   const __bf16* dout;
   const float* lse;
-  float* delta;  // workspace: Delta per row
-  float* lse2;   // workspace: lse * log2(e) per row
+  float* ndelta;  // workspace: -Delta per row
+  float* nls;     // workspace: -lse / scale per row
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
@@ -62,7 +64,7 @@ struct BwdParams {
   float scale;
 };
 
-// ---- delta: Delta_i = sum_d dO_id O_id and lse_i * log2(e), one row per D/8 lanes.
+// ---- delta: -Delta_i = -sum_d dO_id O_id and -lse_i / scale, one row per D/8 lanes.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const BwdParams p) {
   constexpr int kLanesPerRow = D / 8;
@@ -79,8 +81,8 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const BwdParams p) 
 #pragma unroll
   for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kLanesPerRow);
   if (row < p.rows && part == 0) {
-    p.delta[row] = acc;
-    p.lse2[row] = p.lse[row] * kLog2e;
+    p.ndelta[row] = -acc;
+    p.nls[row] = -p.lse[row] / p.scale;
   }
 }
 
@@ -90,12 +92,15 @@ __device__ inline int remap_block(int g, int remap) {
   return (g & 7) * per_xcd + (g >> 3);
 }
 
-// Row-read base of an MFMA A operand from a swz-permuted [rows, D] tile: lane (m + 32h)
-// reads logical chunk 2st + h of row m; the permutation depends on m only.
+// Row-read address of an MFMA A operand from a swz-permuted [rows, D] tile: lane (m + 32h)
+// reads logical chunk 2st + h of row m, at m*2D + 16((2st + h) ^ swz(m)). Since 2st and h
+// occupy disjoint bits, that is row_read_base(m, h) ^ 32st: one base register per lane
+// and an XOR per read instead of D/16 registers.
 template <int D>
-__device__ inline int row_read_addr(int col, int hi, int st) {
-  return col * (2 * D) + 16 * ((2 * st + hi) ^ swz<D>(col));
+__device__ inline int row_read_base(int col, int hi) {
+  return col * (2 * D) + 16 * (hi ^ swz<D>(col));
 }
+__device__ inline int row_read_addr(int base, int st) { return base ^ (32 * st); }
 // Transposed-read base (ds_read_b64_tr_b16) of 4x16 blocks from a swz-permuted
 // [rows, D] tile, for output column block d and row half u: in each 16-lane group the
 // source lane jj supplies 8 bytes of row 8u + 4h + (jj >> 2) at logical column
@@ -136,12 +141,19 @@ __device__ inline void store_rows(__bf16* out_row, const f32x16 (&acc)[D / 32], 
 }
 
 // ---- dkdv: workgroup = 128 keys, wave = 32 keys; query tiles of 64 stream through LDS.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// PART selects the outputs: kDkDv both; kDvOnly dV (no dP, dS or V operand); kDkOnly dK.
+// Both at once need 32 + 32 registers of K and V operands and 64 + 64 of accumulators at
+// D = 128, which leaves too few of a wave's 256 (two waves per SIMD) for the rest, so
+// D = 128 runs the two parts as two kernels (S is formed in both) and D = 64 runs one.
+constexpr int kDkDv = 0, kDvOnly = 1, kDkOnly = 2;
+template <int D, bool CAUSAL, int PART>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(const BwdParams p) {
+  constexpr bool kDv = PART != kDkOnly;
+  constexpr bool kDk = PART != kDvOnly;
   constexpr int RB = 2 * D;
   constexpr int kTileBytes = kTile * RB;
-  constexpr int kSlot = 2 * kTileBytes + 2 * kTile * 4;  // Q, dO, lse2, Delta
+  constexpr int kSlot = 2 * kTileBytes + 2 * kTile * 4;  // Q, dO, -lse/scale, -Delta
   __shared__ __attribute__((aligned(1024))) char smem[2 * kSlot];
 
   const int tid = threadIdx.x;
@@ -167,7 +179,7 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       kf[s] = ks[2 * s];
-      vf[s] = vs[2 * s];
+      if (kDk) vf[s] = vs[2 * s];
     }
   }
   f32x16 dv[D / 32], dk[D / 32];
@@ -180,8 +192,8 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
   const uint32_t head_bytes = (uint32_t)N * RB;
   const i32x4 qrsrc = make_rsrc(p.q + head, head_bytes);
   const i32x4 orsrc = make_rsrc(p.dout + head, head_bytes);
-  const i32x4 lrsrc = make_rsrc(p.lse2 + (size_t)bh * N, (uint32_t)N * 4u);
-  const i32x4 drsrc = make_rsrc(p.delta + (size_t)bh * N, (uint32_t)N * 4u);
+  const i32x4 lrsrc = make_rsrc(p.nls + (size_t)bh * N, (uint32_t)N * 4u);
+  const i32x4 drsrc = make_rsrc(p.ndelta + (size_t)bh * N, (uint32_t)N * 4u);
   const uint32_t smem_lds = lds_address(smem);
 
   // query tiles: causal workgroups start at their first key
@@ -192,12 +204,10 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
     copy_tile<D, kTile, kWaves>(qrsrc, qt * kTile, N, base, wave, lane);
     copy_tile<D, kTile, kWaves>(orsrc, qt * kTile, N, base + kTileBytes, wave, lane);
     if (wave == 0) copy_vec64(lrsrc, qt * kTile, N, base + 2 * kTileBytes, lane);
-    if (wave == 1) copy_vec64(drsrc, qt * kTile, N, base + 2 * kTileBytes + kTile * 4, lane);
+    if (kDk && wave == 1) copy_vec64(drsrc, qt * kTile, N, base + 2 * kTileBytes + kTile * 4, lane);
   };
 
-  int ra[D / 16];
-#pragma unroll
-  for (int st = 0; st < D / 16; ++st) ra[st] = row_read_addr<D>(col, hi, st);
+  const int rbase = row_read_base<D>(col, hi);
   int ta[D / 32][2];
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) {
@@ -212,27 +222,35 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
     if (qt + 1 < qt_end) load(qt + 1, slot ^ 1);
     const int qs = slot * kSlot;                  // Q tile
     const int os = qs + kTileBytes;               // dO tile
-    const int ls = qs + 2 * kTileBytes;           // lse2
-    const int ds = ls + kTile * 4;                // Delta
+    const int ls = qs + 2 * kTileBytes;           // -lse / scale
+    const int ds = ls + kTile * 4;                // -Delta
 #pragma unroll
     for (int b = 0; b < kTile / kBlk; ++b) {
       const int qb0 = qt * kTile + b * kBlk;  // first query of this block
       if (CAUSAL && qb0 + kBlk - 1 < k0) continue;  // every query precedes every key
       if (k0 >= N) continue;                        // wave past the last key
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(smem + qs + b * kBlk * RB + ra[st]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[st], s, 0, 0, 0);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(smem + os + b * kBlk * RB + ra[st]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[st], dp, 0, 0, 0);
-      }
-      // register r holds query qb0 + 8(r/4) + 4h + r%4 of key `key`
-      f32x4 l2[4], dl[4];
+      // register r holds query qb0 + 8(r/4) + 4h + r%4 of key `key`; the accumulators
+      // start at -lse / scale and -Delta of their query
+      f32x16 s, dp;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        l2[g4] = *reinterpret_cast<const f32x4*>(smem + ls + (b * kBlk + 8 * g4 + 4 * hi) * 4);
-        dl[g4] = *reinterpret_cast<const f32x4*>(smem + ds + (b * kBlk + 8 * g4 + 4 * hi) * 4);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(smem + ls + (b * kBlk + 8 * g4 + 4 * hi) * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[4 * g4 + i] = a[i];
+        if (kDk) {
+          const f32x4 d = *reinterpret_cast<const f32x4*>(smem + ds + (b * kBlk + 8 * g4 + 4 * hi) * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dp[4 * g4 + i] = d[i];
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(smem + qs + b * kBlk * RB + row_read_addr(rbase, st));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[st], s, 0, 0, 0);
+        if (kDk) {
+          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(smem + os + b * kBlk * RB + row_read_addr(rbase, st));
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vf[st], dp, 0, 0, 0);
+        }
       }
       const bool need_mask = (CAUSAL && qb0 < k0 + kBlk - 1) || (qb0 + kBlk > N);
       // visible iff query < N and (causal) key <= query: query index minus this lane's
@@ -242,31 +260,34 @@ void attn_bwd_dkdv_kernel(const BwdParams p) {
       bf16x8 pb[2], sb[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -l2[r >> 2][r & 3]));
+        float pr = __builtin_amdgcn_exp2f(s[r] * p.c);
         if (need_mask) {
           const int qo = 8 * (r >> 2) + (r & 3);
           if (qo < lo_lim || qo >= hi_lim) pr = 0.f;
         }
-        const float dsr = pr * (dp[r] - dl[r >> 2][r & 3]);
-        pb[r >> 3][r & 7] = (__bf16)pr;
-        sb[r >> 3][r & 7] = (__bf16)dsr;
+        if (kDv) pb[r >> 3][r & 7] = (__bf16)pr;
+        if (kDk) sb[r >> 3][r & 7] = (__bf16)(pr * dp[r]);
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 queries (two k-steps of 16)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int d = 0; d < D / 32; ++d) {
-          const bf16x8 oa = tr_frag<D>(smem, os, ta[d], b * kBlk + 16 * st);
-          dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pb[st], dv[d], 0, 0, 0);
-          const bf16x8 qa = tr_frag<D>(smem, qs, ta[d], b * kBlk + 16 * st);
-          dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb[st], dk[d], 0, 0, 0);
+          if (kDv) {
+            const bf16x8 oa = tr_frag<D>(smem, os, ta[d], b * kBlk + 16 * st);
+            dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, pb[st], dv[d], 0, 0, 0);
+          }
+          if (kDk) {
+            const bf16x8 qa = tr_frag<D>(smem, qs, ta[d], b * kBlk + 16 * st);
+            dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, sb[st], dk[d], 0, 0, 0);
+          }
         }
       }
     }
   }
   if (key < N) {
-    store_rows<D>(p.dv + head + (size_t)key * D, dv, hi, 1.f);
-    store_rows<D>(p.dk + head + (size_t)key * D, dk, hi, p.scale);
+    if (kDv) store_rows<D>(p.dv + head + (size_t)key * D, dv, hi, 1.f);
+    if (kDk) store_rows<D>(p.dk + head + (size_t)key * D, dk, hi, p.scale);
   }
 }
 
@@ -296,7 +317,7 @@ void attn_bwd_dq_kernel(const BwdParams p) {
 
   // Q and dO as B operands (lane = query, k = D index 16st + 8h .. +7)
   bf16x8 qf[D / 16], of[D / 16];
-  float l2 = 0.f, dl = 0.f;
+  float nls = 0.f, ndl = 0.f;
   {
     const int r = min(qrow, N - 1);
     const bf16x8* qs = reinterpret_cast<const bf16x8*>(p.q + head + (size_t)r * D) + hi;
@@ -306,8 +327,8 @@ void attn_bwd_dq_kernel(const BwdParams p) {
       qf[s] = qs[2 * s];
       of[s] = os[2 * s];
     }
-    l2 = p.lse2[(size_t)bh * N + r];
-    dl = p.delta[(size_t)bh * N + r];
+    nls = p.nls[(size_t)bh * N + r];
+    ndl = p.ndelta[(size_t)bh * N + r];
   }
   f32x16 dq[D / 32];
 #pragma unroll
@@ -327,9 +348,7 @@ void attn_bwd_dq_kernel(const BwdParams p) {
     copy_tile<D, kTile, kWaves>(vrsrc, t * kTile, N, base + kTileBytes, wave, lane);
   };
 
-  int ra[D / 16];
-#pragma unroll
-  for (int st = 0; st < D / 16; ++st) ra[st] = row_read_addr<D>(col, hi, st);
+  const int rbase = row_read_base<D>(col, hi);
   int ta[D / 32][2];
 #pragma unroll
   for (int d = 0; d < D / 32; ++d) {
@@ -348,12 +367,13 @@ void attn_bwd_dq_kernel(const BwdParams p) {
     for (int j = 0; j < kTile / kBlk; ++j) {
       const int kb0 = t * kTile + j * kBlk;  // first key of this block
       if (q0 >= N || kb0 >= wave_kv_end) continue;
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // the accumulators start at -lse / scale and -Delta of this lane's query
+      f32x16 s = f32x16{} + nls, dp = f32x16{} + ndl;
 #pragma unroll
       for (int st = 0; st < D / 16; ++st) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(smem + ks + j * kBlk * RB + ra[st]);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(smem + ks + j * kBlk * RB + row_read_addr(rbase, st));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[st], s, 0, 0, 0);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(smem + vs + j * kBlk * RB + ra[st]);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(smem + vs + j * kBlk * RB + row_read_addr(rbase, st));
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, of[st], dp, 0, 0, 0);
       }
       // register r holds key kb0 + 8(r/4) + 4h + r%4 of query qrow
@@ -362,9 +382,9 @@ void attn_bwd_dq_kernel(const BwdParams p) {
       bf16x8 sb[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -l2));
+        float pr = __builtin_amdgcn_exp2f(s[r] * p.c);
         if (need_mask && 8 * (r >> 2) + (r & 3) >= lim) pr = 0.f;
-        sb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - dl));
+        sb[r >> 3][r & 7] = (__bf16)(pr * dp[r]);
       }
       // dQ^T += K^T dS^T over the block's 32 keys
 #pragma unroll
@@ -387,10 +407,20 @@ void launch_bwd(int causal, int B, int H, hipStream_t s, const BwdParams& p) {
                      block, 0, s, p);
   const dim3 grid((unsigned)(B * H * p.n_wg_tiles));
   if (causal) {
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), grid, block, 0, s, p);
+    if constexpr (D == 64) {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, kDkDv>), grid, block, 0, s, p);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, kDvOnly>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, kDkOnly>), grid, block, 0, s, p);
+    }
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), grid, block, 0, s, p);
   } else {
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), grid, block, 0, s, p);
+    if constexpr (D == 64) {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, kDkDv>), grid, block, 0, s, p);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, kDvOnly>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, kDkOnly>), grid, block, 0, s, p);
+    }
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), grid, block, 0, s, p);
   }
 }
@@ -435,8 +465,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   p.o = static_cast<const __bf16*>(o);
   p.dout = static_cast<const __bf16*>(dout);
   p.lse = lse;
-  p.delta = static_cast<float*>(workspace);
-  p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+  p.ndelta = static_cast<float*>(workspace);
+  p.nls = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                     round_up((size_t)rows * sizeof(float), 256));
   p.dq = static_cast<__bf16*>(dq);
   p.dk = static_cast<__bf16*>(dk);
