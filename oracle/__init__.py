@@ -9,13 +9,16 @@ code. Modules:
   brute      pure-Python loops with math.fsum, for tiny shapes
   online     the pages' tiled online-softmax recurrence in float64 (to pin the identity)
   backward   the gradients dQ, dK, dV of the forward definition, by the chain rule
+  decode     few queries against a long key/value sequence (bottom-right causal mask)
 
-Every function here is pinned by ``tests/test_oracle.py`` and ``tests/test_oracle_bwd.py``
+Every function here is pinned by ``tests/test_oracle.py``, ``tests/test_oracle_bwd.py`` and
+``tests/test_oracle_decode.py``
 against closed forms, invariants, a hand-derived worked example, brute force and finite
 differences.
 """
 from .attention import attention_fwd, attention_head, attention_probs, attention_rows
 from .backward import attention_bwd, attention_bwd_head
+from .decode import attention_decode
 from .brute import attention_brute
 from .online import attention_online
 
@@ -28,4 +31,5 @@ __all__ = [
     "attention_online",
     "attention_bwd",
     "attention_bwd_head",
+    "attention_decode",
 ]
