@@ -6,13 +6,17 @@ device pointers and the current HIP stream. Every step of the computation runs i
 library's HIP kernels; if the library is missing this module raises instead of computing
 anything itself.
 
-C entry points (declared in include/attn_fwd.h and include/attn_bwd.h):
+C entry points (declared in include/attn_fwd.h, include/attn_bwd.h, include/attn_decode.h):
   int attn_fwd(q, k, v, o, lse, B, H, N, D, causal, scale, stream)
   const char* attn_fwd_strerror(int code)
   size_t attn_bwd_workspace_bytes(B, H, N)
   int attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
                B, H, N, D, causal, scale, stream)
   const char* attn_bwd_strerror(int code)
+  size_t attn_decode_workspace_bytes(B, H, Nq, Nk, D)
+  int attn_decode(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, D, causal,
+                  scale, stream)
+  const char* attn_decode_strerror(int code)
 """
 from __future__ import annotations
 
@@ -73,6 +77,12 @@ def load_library():
         lib.attn_bwd.restype = ci
         lib.attn_bwd_strerror.argtypes = [ci]
         lib.attn_bwd_strerror.restype = ctypes.c_char_p
+        lib.attn_decode_workspace_bytes.argtypes = [ci] * 5
+        lib.attn_decode_workspace_bytes.restype = sz
+        lib.attn_decode.argtypes = [vp] * 6 + [sz] + [ci] * 6 + [ctypes.c_float, vp]
+        lib.attn_decode.restype = ci
+        lib.attn_decode_strerror.argtypes = [ci]
+        lib.attn_decode_strerror.restype = ctypes.c_char_p
         _lib = lib
         return lib
 
@@ -213,3 +223,63 @@ def attn_bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = 
             raise ValueError(f"attn_bwd rejected its arguments (code {code}): {msg}")
         raise AttnBwdError(code, msg)
     return tuple(outs)
+
+
+class AttnDecodeError(RuntimeError):
+    """A nonzero return code from attn_decode."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"attn_decode failed with code {code}: {message}")
+        self.code = code
+
+
+def decode_workspace_bytes(B: int, H: int, Nq: int, Nk: int, D: int) -> int:
+    return int(load_library().attn_decode_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(D)))
+
+
+def attn_decode(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+                workspace=None, stream=None):
+    """Decode-shaped attention on the GPU: q [B, H, Nq, D] (Nq <= 32) against k, v
+    [B, H, Nk, D], all contiguous bfloat16 CUDA tensors. Causal queries are the last Nq
+    positions. Returns (O bfloat16 [B, H, Nq, D], lse float32 [B, H, Nq]); the workspace
+    (uint8 CUDA tensor, 256-byte aligned) is allocated when not given."""
+    import torch
+
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(name, t)
+    if k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError(f"shapes do not match: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if len({t.device for t in (q, k, v)}) != 1:
+        raise ValueError("q, k, v must be on the same device")
+    B, H, Nq, D = (int(x) for x in q.shape)
+    Nk = int(k.shape[2])
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_bf16("out", out)
+        if out.shape != q.shape or out.device != q.device:
+            raise ValueError("out must be shaped like q on q's device")
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous()
+          or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, H, Nq] on q's device")
+    lib = load_library()
+    need = int(lib.attn_decode_workspace_bytes(B, H, Nq, Nk, D))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif (workspace.dtype != torch.uint8 or workspace.device != q.device
+          or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+    handle = _stream_handle(stream, q.device)
+    code = lib.attn_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                           workspace.data_ptr(), workspace.numel(), B, H, Nq, Nk, D,
+                           int(bool(causal)), float(scale), handle)
+    if code != ATTN_FWD_OK:
+        msg = lib.attn_decode_strerror(code).decode()
+        if code in (ATTN_FWD_EINVAL, ATTN_FWD_EUNSUPPORTED, ATTN_FWD_EALIGN, ATTN_BWD_EWORKSPACE):
+            raise ValueError(f"attn_decode rejected its arguments (code {code}): {msg}")
+        raise AttnDecodeError(code, msg)
+    return out, lse

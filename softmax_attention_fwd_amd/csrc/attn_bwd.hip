@@ -86,60 +86,6 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const BwdParams p) 
   }
 }
 
-__device__ inline int remap_block(int g, int remap) {
-  if (!remap) return g;
-  const int per_xcd = gridDim.x >> 3;
-  return (g & 7) * per_xcd + (g >> 3);
-}
-
-// Row-read address of an MFMA A operand from a swz-permuted [rows, D] tile: lane (m + 32h)
-// reads logical chunk 2st + h of row m, at m*2D + 16((2st + h) ^ swz(m)). Since 2st and h
-// occupy disjoint bits, that is row_read_base(m, h) ^ 32st: one base register per lane
-// and an XOR per read instead of D/16 registers.
-template <int D>
-__device__ inline int row_read_base(int col, int hi) {
-  return col * (2 * D) + 16 * (hi ^ swz<D>(col));
-}
-__device__ inline int row_read_addr(int base, int st) { return base ^ (32 * st); }
-// Transposed-read base (ds_read_b64_tr_b16) of 4x16 blocks from a swz-permuted
-// [rows, D] tile, for output column block d and row half u: in each 16-lane group the
-// source lane jj supplies 8 bytes of row 8u + 4h + (jj >> 2) at logical column
-// 32d + 16(grp & 1) + 4(jj & 3); the instruction hands lane jj column jj of that 4-row
-// block. The permutation depends on the row mod 16, so row offsets that are multiples of
-// 16 are added as constants, while the two 8-row halves need bases of their own.
-template <int D>
-__device__ inline int tr_read_addr(int lane, int d, int u) {
-  const int jj = lane & 15, grp = lane >> 4, hi = lane >> 5;
-  const int row = 8 * u + 4 * hi + (jj >> 2);
-  const int chunk = 4 * d + 2 * (grp & 1) + ((jj >> 1) & 1);
-  return row * (2 * D) + 16 * (chunk ^ swz<D>(row)) + 8 * (jj & 1);
-}
-// A operand of MFMA k-step over rows row0..row0+15 (row0 a multiple of 16) for output
-// columns 32d.. from the tile at smem + tile: rows row0 + 4h + {0..3} (low four k) and
-// row0 + 8 + 4h + {0..3} (high four k), column 32d + lane % 32.
-template <int D>
-__device__ inline bf16x8 tr_frag(const char* smem, int tile, const int (&addr)[2], int row0) {
-  const char* base = smem + tile + row0 * (2 * D);
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + addr[0]));
-  const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + addr[1]));
-  return __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Store a D x 32 fp32 accumulator (transposed layout: register r of block d holds column
-// 32d + 8(r/4) + 4h + r%4 of row `row`) as bf16 row `row` of out, times s.
-template <int D>
-__device__ inline void store_rows(__bf16* out_row, const f32x16 (&acc)[D / 32], int hi, float s) {
-#pragma unroll
-  for (int d = 0; d < D / 32; ++d)
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      bf16x4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (__bf16)(acc[d][4 * j4 + i] * s);
-      *reinterpret_cast<bf16x4*>(out_row + 32 * d + 8 * j4 + 4 * hi) = w;
-    }
-}
-
 // ---- dkdv: workgroup = 128 keys, wave = 32 keys; query tiles of 64 stream through LDS.
 // PART selects the outputs: kDkDv both; kDvOnly dV (no dP, dS or V operand); kDkOnly dK.
 // Both at once need 32 + 32 registers of K and V operands and 64 + 64 of accumulators at

@@ -94,3 +94,62 @@ def make_dout(B: int, H: int, N: int, D: int, seed: int, sigma: float = 1.0):
     if sigma != 1.0:
         x.mul_(sigma)
     return x.to(torch.bfloat16).contiguous()
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """A decode-shaped problem: Nq queries against an Nk-long key/value sequence."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    D: int
+    causal: bool
+    sigma_qk: float = 1.0
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def kv_bytes(self) -> int:
+        """K and V read once (bf16): the bytes that bound the kernel."""
+        return 2 * self.B * self.H * self.Nk * self.D * 2
+
+    @property
+    def hbm_bytes(self) -> int:
+        """Algorithmic HBM bytes: K, V, Q read once, O (bf16) and lse (fp32) written."""
+        return self.kv_bytes + 2 * self.B * self.H * self.Nq * self.D * 2 + 4 * self.B * self.H * self.Nq
+
+    def describe(self) -> str:
+        c = "causal" if self.causal else "non-causal"
+        return f"B{self.B} H{self.H} Nq{self.Nq} Nk{self.Nk} D{self.D} {c}"
+
+
+# Decode shapes built from the forward workloads' heads and lengths (the pages give no
+# inference shapes): one new token per sequence against the KV cache of workload 3's
+# batch, 8 speculative tokens against workload 5's long peaky sequence, and one token
+# against a 128K-token cache.
+DECODE_WORKLOADS = {
+    1: DecodeWorkload("d1_b16h16q1k4096d128", 16, 16, 1, 4096, 128, True, seed=2001),
+    2: DecodeWorkload("d2_b1h32q8k16384d128", 1, 32, 8, 16384, 128, True, sigma_qk=2.0, seed=2002),
+    3: DecodeWorkload("d3_b4h8q1k131072d128", 4, 8, 1, 131072, 128, True, seed=2003),
+}
+
+
+def decode_inputs(w: DecodeWorkload):
+    """Q [B, H, Nq, D], K, V [B, H, Nk, D] (CPU bfloat16) of a decode workload: one
+    generator seeded with w.seed draws Q, then K, then V (standard normals; Q and K times
+    sigma_qk), rounded to bfloat16."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(w.seed))
+    out = []
+    for shape, sigma in (((w.B, w.H, w.Nq, w.D), w.sigma_qk), ((w.B, w.H, w.Nk, w.D), w.sigma_qk),
+                         ((w.B, w.H, w.Nk, w.D), 1.0)):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        if sigma != 1.0:
+            x.mul_(sigma)
+        out.append(x.to(torch.bfloat16).contiguous())
+    return tuple(out)

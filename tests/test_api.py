@@ -43,7 +43,8 @@ def declared_codes(prefix="ATTN_FWD_"):
 
 def test_header_declares_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_strerror", "attn_bwd_workspace_bytes",
-                                    "attn_fwd", "attn_fwd_strerror"]
+                                    "attn_decode", "attn_decode_strerror",
+                                    "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_strerror"]
 
 
 def test_exports_every_declared_symbol(lib):
@@ -170,3 +171,37 @@ def test_bwd_binding_rejects_cpu_tensors():
     lse = torch.zeros(1, 1, 8)
     with pytest.raises(ValueError, match="GPU"):
         binding.attn_bwd(q, q, q, q, q, lse)
+
+
+def test_decode_codes_and_strerror(lib):
+    codes = declared_codes("ATTN_DECODE_")
+    assert codes == {"ATTN_DECODE_OK": 0, "ATTN_DECODE_EINVAL": -1, "ATTN_DECODE_EUNSUPPORTED": -2,
+                     "ATTN_DECODE_EALIGN": -3, "ATTN_DECODE_ELAUNCH": -4, "ATTN_DECODE_EWORKSPACE": -5}
+    msgs = {lib.attn_decode_strerror(c).decode() for c in codes.values()}
+    assert len(msgs) == len(codes) and "unknown error code" not in msgs
+
+
+def test_decode_workspace_bytes(lib):
+    # 256 heads -> 4 key chunks each; partial O (fp32) and lse per chunk and query
+    assert lib.attn_decode_workspace_bytes(16, 16, 1, 4096, 128) == 4 * 256 * 128 * 4 + 4096
+    assert lib.attn_decode_workspace_bytes(1, 1, 33, 100, 64) == 0   # Nq > 32
+    assert lib.attn_decode_workspace_bytes(1, 1, 1, 100, 96) == 0    # unsupported D
+    assert lib.attn_decode_workspace_bytes(0, 1, 1, 100, 64) == 0
+
+
+def call_dec(lib, q=A, k=A, v=A, o=A, lse=A, ws=W, ws_bytes=1 << 24, B=1, H=1, Nq=1, Nk=128,
+             D=64, causal=0, scale=0.125):
+    return lib.attn_decode(q, k, v, o, lse, ws, ws_bytes, B, H, Nq, Nk, D, causal,
+                           ctypes.c_float(scale), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(v=None), -1), (dict(lse=None), -1), (dict(ws=None), -1),
+    (dict(Nq=0), -1), (dict(Nk=0), -1), (dict(B=0), -1), (dict(causal=2), -1),
+    (dict(causal=1, Nq=8, Nk=4), -1), (dict(scale=0.0), -1), (dict(scale=math.inf), -1),
+    (dict(D=96), -2), (dict(Nq=33), -2), (dict(Nk=1 << 24, D=128), -1),
+    (dict(ws_bytes=10), -5), (dict(q=A + 8), -3), (dict(o=A + 2), -3), (dict(lse=A + 1), -3),
+    (dict(ws=W + 64), -3),
+])
+def test_decode_invalid_arguments_rejected(lib, kw, code):
+    assert call_dec(lib, **kw) == code
