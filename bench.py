@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
 """Attention forward throughput on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload 3] [--gpus 1] [--op fwd|bwd]
+    python bench.py [--steps K] [--warmup W] [--workload 3] [--gpus 1] [--op fwd|bwd|decode]
 
 One step = one attn_fwd call (the whole fused forward: K/V streaming, both contractions,
 online softmax, epilogue) over the workload's full tensors, already resident in HBM; with
---op bwd, one attn_bwd call (its three kernels: Delta, dK/dV, dQ) on the same shapes.
+--op bwd, one attn_bwd call (its kernels: Delta, dK/dV, dQ) on the same shapes; with
+--op decode, one attn_decode call (split kernel + merge) on a decode workload (1..3:
+few queries against a long KV cache), reported in GB/s of K and V read against HBM.
 The default workload is B16 H16 N4096 D128 non-causal with bf16 inputs. Prints ONE JSON
 line on stdout; details go to stderr.
 
@@ -33,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X bf16 dense MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "softmax_attention_fwd_amd", "csrc", "attn_fwd.hip")
 
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (separate
@@ -115,6 +118,142 @@ def cpu_baseline(w, q, k, v, budget_s: float, do=None):
     }
 
 
+def time_steps(step, stream, steps: int, warmup: int):
+    """Run warmup steps, then time `steps` steps with per-step HIP events and one span
+    pair on `stream`. Returns (span_ms, per-step ms list, wall seconds)."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {warmup} done; timing {steps} steps")
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    span0 = torch.cuda.Event(enable_timing=True)
+    span1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    span0.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    span1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return span0.elapsed_time(span1), [a.elapsed_time(b) for a, b in zip(starts, ends)], wall
+
+
+def decode_cpu_baseline(w, q, k, v, budget_s: float):
+    """Time the fp64 decode oracle on whole heads, one head per host core, in GB/s of the
+    workload's algorithmic bytes per head."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    nh = w.B * w.H
+    heads = min(nh, cores)
+    per_head = w.hbm_bytes / nh
+    qs = [q.view(nh, 1, 1, w.Nq, w.D)[i].double().numpy() for i in range(heads)]
+    ks = [k.view(nh, 1, 1, w.Nk, w.D)[i].double().numpy() for i in range(heads)]
+    vs = [v.view(nh, 1, 1, w.Nk, w.D)[i].double().numpy() for i in range(heads)]
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        done = 0
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=heads) as ex:
+            while True:
+                list(ex.map(lambda i: oracle.attention_decode(qs[i], ks[i], vs[i], w.causal, w.scale),
+                            range(heads)))
+                done += heads
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    return {
+        "value": round(done * per_head / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{done} head-passes (decode) of {w.describe()} (first {heads} heads, "
+                   f"{done * per_head / 1e9:.3f} GB of K/V/Q/O, fp64 numpy, one head per thread) "
+                   f"in {dt:.1f} s"),
+    }
+
+
+def run_decode(args) -> int:
+    import torch
+
+    from softmax_attention_fwd_amd import attn_decode, decode_workspace_bytes
+    from softmax_attention_fwd_amd.inputs import DECODE_WORKLOADS, decode_inputs
+
+    w = DECODE_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"[bench] decode workload {args.workload}: {w.describe()}; generating inputs (seed {w.seed})")
+    q, k, v = decode_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(decode_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.D), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        attn_decode(qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws,
+                    stream=stream)
+
+    total_ms, launch_ms, wall = time_steps(step, stream, args.steps, args.warmup)
+    mean_launch = statistics.fmean(launch_ms)
+    value = w.hbm_bytes * args.steps / (total_ms * 1e-3) / 1e9
+    achieved = w.hbm_bytes / (mean_launch * 1e-3) / 1e9
+    log(f"[bench] span {total_ms:.3f} ms for {args.steps} steps; launch median "
+        f"{statistics.median(launch_ms):.4f} ms; {value:.1f} GB/s whole-job, {achieved:.1f} GB/s "
+        f"per call = {100 * achieved / PEAK_HBM_GBS:.1f}% of HBM peak")
+    result = {
+        "metric": "attention decode (split-KV) GB/s of K, V, Q, O and lse against HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q, K, V)",
+        "config": {"workload": w.name, "op": "decode", "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk,
+                   "D": w.D, "causal": w.causal, "scale": w.scale, "parallelism": "single GPU"},
+        "launch_ms": {"mean": round(mean_launch, 5), "median": round(statistics.median(launch_ms), 5),
+                      "min": round(min(launch_ms), 5), "max": round(max(launch_ms), 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "traffic_algorithmic": w.hbm_bytes},
+        "cpu_baseline": None,
+    }
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 3 x 512 MiB device-to-device")
+        del src, dst
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the fp64 decode oracle on host cores (~{args.cpu_seconds:.0f} s budget)")
+        result["cpu_baseline"] = decode_cpu_baseline(w, q, k, v, args.cpu_seconds)
+        log(f"[bench] cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,8 +261,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=40,
                     help="untimed launches first; the shader clock settles over ~20 launches")
     ap.add_argument("--workload", type=int, default=3, help="1..5 (default 3)")
-    ap.add_argument("--op", choices=("fwd", "bwd"), default="fwd",
-                    help="the forward (default, the headline metric) or the backward pass")
+    ap.add_argument("--op", choices=("fwd", "bwd", "decode"), default="fwd",
+                    help="the forward (default, the headline metric), the backward pass, or "
+                         "the decode-shaped split-KV forward")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -140,6 +280,9 @@ def main() -> int:
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
+
+    if args.op == "decode":
+        return run_decode(args)
 
     import torch
 
@@ -174,28 +317,7 @@ def main() -> int:
             attn_bwd(qd, kd, vd, o, dod, lse, causal=w.causal, scale=w.scale, dq=grads[0],
                      dk=grads[1], dv=grads[2], workspace=ws, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    span0 = torch.cuda.Event(enable_timing=True)
-    span1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    span0.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    span1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-
-    total_ms = span0.elapsed_time(span1)
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    total_ms, launch_ms, wall = time_steps(step, stream, args.steps, args.warmup)
     mean_launch = statistics.fmean(launch_ms)
     ms_per_step = total_ms / args.steps
     value = flops * args.steps / (total_ms * 1e-3) / 1e12
