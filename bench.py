@@ -7,7 +7,8 @@ One step = one attn_fwd call (the whole fused forward: K/V streaming, both contr
 online softmax, epilogue) over the workload's full tensors, already resident in HBM; with
 --op bwd, one attn_bwd call (its kernels: Delta, dK/dV, dQ) on the same shapes; with
 --op decode, one attn_decode call (split kernel + merge) on a decode workload (1..3:
-few queries against a long KV cache), reported in GB/s of K and V read against HBM.
+few queries against a long KV cache), reported in GB/s of K and V read against HBM; with
+--op gemm, one C = A B^T (bf16) of --gemm-shape M,N,K, in TFLOP/s (2*M*N*K).
 The default workload is B16 H16 N4096 D128 non-causal with bf16 inputs. Prints ONE JSON
 line on stdout; details go to stderr.
 
@@ -254,6 +255,70 @@ def run_decode(args) -> int:
     return 0
 
 
+def run_gemm(args) -> int:
+    import torch
+
+    from softmax_attention_fwd_amd import gemm_nt
+
+    M, N, K = (int(x) for x in args.gemm_shape.split(","))
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(3001)
+    a = torch.randn((M, K), generator=g).to(torch.bfloat16)
+    b = torch.randn((N, K), generator=g).to(torch.bfloat16)
+    ad, bd = a.to(dev), b.to(dev)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    flops = 2.0 * M * N * K
+    log(f"[bench] gemm C = A B^T, M {M} N {N} K {K} (bf16, seed 3001)")
+
+    def step():
+        gemm_nt(ad, bd, out=c, stream=stream)
+
+    total_ms, launch_ms, wall = time_steps(step, stream, args.steps, args.warmup)
+    mean_launch = statistics.fmean(launch_ms)
+    value = flops * args.steps / (total_ms * 1e-3) / 1e12
+    achieved = flops / (mean_launch * 1e-3) / 1e12
+    log(f"[bench] {value:.1f} TFLOP/s whole-job; kernel {achieved:.1f} TFLOP/s = "
+        f"{100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 dense peak")
+    result = {
+        "metric": "bf16 GEMM C = A B^T TFLOP/s (2*M*N*K) and % of bf16 MFMA peak",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 A, B)",
+        "config": {"workload": f"gemm_m{M}n{N}k{K}", "op": "gemm", "M": M, "N": N, "K": K,
+                   "parallelism": "single GPU"},
+        "launch_ms": {"mean": round(mean_launch, 5), "median": round(statistics.median(launch_ms), 5),
+                      "min": round(min(launch_ms), 5), "max": round(max(launch_ms), 5)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "traffic_algorithmic": 2 * (M * K + N * K + M * N)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        rows = max(1, min(M, 256))
+        an, bn = a[:rows].double().numpy(), b.double().numpy()
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle.gemm_nt(an, bn)
+            done += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(done * 2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{done} products of the first {rows} rows of A with B (fp64 numpy, BLAS threads "
+                      f"as numpy sets them) in {dt:.1f} s"}
+        log(f"[bench] cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,9 +326,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=40,
                     help="untimed launches first; the shader clock settles over ~20 launches")
     ap.add_argument("--workload", type=int, default=3, help="1..5 (default 3)")
-    ap.add_argument("--op", choices=("fwd", "bwd", "decode"), default="fwd",
+    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "gemm"), default="fwd",
                     help="the forward (default, the headline metric), the backward pass, or "
-                         "the decode-shaped split-KV forward")
+                         "the decode-shaped split-KV forward, or the plain GEMM")
+    ap.add_argument("--gemm-shape", default="8192,8192,8192", help="M,N,K for --op gemm")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -283,6 +349,8 @@ def main() -> int:
 
     if args.op == "decode":
         return run_decode(args)
+    if args.op == "gemm":
+        return run_gemm(args)
 
     import torch
 

@@ -6,7 +6,7 @@ device pointers and the current HIP stream. Every step of the computation runs i
 library's HIP kernels; if the library is missing this module raises instead of computing
 anything itself.
 
-C entry points (declared in include/attn_fwd.h, include/attn_bwd.h, include/attn_decode.h):
+C entry points (declared in include/attn_fwd.h, attn_bwd.h, attn_decode.h, tile_gemm.h):
   int attn_fwd(q, k, v, o, lse, B, H, N, D, causal, scale, stream)
   const char* attn_fwd_strerror(int code)
   size_t attn_bwd_workspace_bytes(B, H, N)
@@ -17,6 +17,8 @@ C entry points (declared in include/attn_fwd.h, include/attn_bwd.h, include/attn
   int attn_decode(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, D, causal,
                   scale, stream)
   const char* attn_decode_strerror(int code)
+  int gemm_bf16_nt(a, b, c, M, N, K, stream)
+  const char* gemm_strerror(int code)
 """
 from __future__ import annotations
 
@@ -83,6 +85,10 @@ def load_library():
         lib.attn_decode.restype = ci
         lib.attn_decode_strerror.argtypes = [ci]
         lib.attn_decode_strerror.restype = ctypes.c_char_p
+        lib.gemm_bf16_nt.argtypes = [vp, vp, vp, ci, ci, ci, vp]
+        lib.gemm_bf16_nt.restype = ci
+        lib.gemm_strerror.argtypes = [ci]
+        lib.gemm_strerror.restype = ctypes.c_char_p
         _lib = lib
         return lib
 
@@ -283,3 +289,41 @@ def attn_decode(q, k, v, causal: bool = False, scale: float | None = None, out=N
             raise ValueError(f"attn_decode rejected its arguments (code {code}): {msg}")
         raise AttnDecodeError(code, msg)
     return out, lse
+
+
+class GemmError(RuntimeError):
+    """A nonzero return code from gemm_bf16_nt."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"gemm_bf16_nt failed with code {code}: {message}")
+        self.code = code
+
+
+def gemm_nt(a, b, out=None, stream=None):
+    """C = A B^T on the GPU: a [M, K], b [N, K] contiguous bfloat16 CUDA tensors (K and N
+    multiples of 8). Returns C bfloat16 [M, N] (``out`` to write in place)."""
+    import torch
+
+    for name, t in (("a", a), ("b", b)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous 2-D bfloat16 GPU tensor")
+    if a.shape[1] != b.shape[1] or a.device != b.device:
+        raise ValueError(f"a {tuple(a.shape)} and b {tuple(b.shape)} must share K and the device")
+    M, K = (int(x) for x in a.shape)
+    N = int(b.shape[0])
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    elif (tuple(out.shape) != (M, N) or out.dtype != torch.bfloat16 or not out.is_contiguous()
+          or out.device != a.device):
+        raise ValueError("out must be a contiguous bfloat16 [M, N] tensor on a's device")
+    lib = load_library()
+    code = lib.gemm_bf16_nt(a.data_ptr(), b.data_ptr(), out.data_ptr(), M, N, K,
+                            _stream_handle(stream, a.device))
+    if code != ATTN_FWD_OK:
+        msg = lib.gemm_strerror(code).decode()
+        if code in (ATTN_FWD_EINVAL, ATTN_FWD_EALIGN):
+            raise ValueError(f"gemm_bf16_nt rejected its arguments (code {code}): {msg}")
+        raise GemmError(code, msg)
+    return out

@@ -2,9 +2,10 @@
 
     python -m softmax_attention_fwd_amd.build        # or __graft_entry__.build()
 
-The library holds three translation units, each with its kernels and C entry points:
-csrc/attn_fwd.hip (the forward), csrc/attn_bwd.hip (the backward) and
-csrc/attn_decode.hip (the decode-shaped split-KV forward). It is built for
+The library holds four translation units, each with its kernels and C entry points:
+csrc/attn_fwd.hip (the forward), csrc/attn_bwd.hip (the backward),
+csrc/attn_decode.hip (the decode-shaped split-KV forward) and csrc/gemm.hip (the plain
+bf16 matrix product on the same tile layer). It is built for
 gfx950 only, with packed fp32 VALU instructions disabled (the compiler would otherwise
 form v_pk_* fp32 ops from plain float code).
 """
@@ -17,7 +18,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip")]
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "gemm.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libattn_fwd.so")
 ARCH = "gfx950"

@@ -45,13 +45,16 @@ def test_header_declares_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_strerror", "attn_bwd_workspace_bytes",
                                     "attn_decode", "attn_decode_strerror",
                                     "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_strerror"]
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "tile_gemm.h")).read(), flags=re.S)
+    assert sorted(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(gemm_\w+)\s*\(", text, flags=re.M)) == \
+        ["gemm_bf16_nt", "gemm_strerror"]
 
 
 def test_exports_every_declared_symbol(lib):
     import subprocess
     exported = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
                               capture_output=True, text=True, check=True).stdout.split()
-    for name in declared_functions():
+    for name in declared_functions() + ["gemm_bf16_nt", "gemm_strerror"]:
         assert hasattr(lib, name), f"{name} declared in include/ but not exported"
         assert name in exported
 
@@ -205,3 +208,21 @@ def call_dec(lib, q=A, k=A, v=A, o=A, lse=A, ws=W, ws_bytes=1 << 24, B=1, H=1, N
 ])
 def test_decode_invalid_arguments_rejected(lib, kw, code):
     assert call_dec(lib, **kw) == code
+
+
+def test_gemm_codes_and_strerror(lib):
+    text = open(os.path.join(ROOT, "include", "tile_gemm.h")).read()
+    codes = {n: int(v) for n, v in re.findall(r"#define\s+(GEMM_\w+)\s+(-?\d+)", text)}
+    assert codes == {"GEMM_OK": 0, "GEMM_EINVAL": -1, "GEMM_EALIGN": -3, "GEMM_ELAUNCH": -4}
+    msgs = {lib.gemm_strerror(c).decode() for c in codes.values()}
+    assert len(msgs) == len(codes) and "unknown error code" not in msgs
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, A, A, 8, 8, 8), -1), ((A, None, A, 8, 8, 8), -1), ((A, A, None, 8, 8, 8), -1),
+    ((A, A, A, 0, 8, 8), -1), ((A, A, A, 8, 0, 8), -1), ((A, A, A, 8, 8, 0), -1),
+    ((A, A, A, 8, 8, 12), -1), ((A, A, A, 8, 12, 8), -1), ((A, A, A, 1 << 20, 8, 1 << 10), -1),
+    ((A + 8, A, A, 8, 8, 8), -3), ((A, A + 2, A, 8, 8, 8), -3), ((A, A, A + 4, 8, 8, 8), -3),
+])
+def test_gemm_invalid_arguments_rejected(lib, args, code):
+    assert lib.gemm_bf16_nt(*args, None) == code
