@@ -30,12 +30,14 @@ constexpr int kWaveM = 128, kWaveN = 64;
 constexpr int kRowBytes = kTk * 2;              // 128-byte rows of a k slice
 constexpr int kTileBytes = 256 * kRowBytes;     // 32 KiB per operand per stage
 constexpr int kStageBytes = 2 * kTileBytes;
+constexpr int kGroupM = 8;                      // tile rows walked together (L2 reuse)
 
 struct GemmParams {
   const __bf16* a;
   const __bf16* b;
   __bf16* c;
   int M, N, K;
+  int tiles_m;  // ceil(M / kTm)
   int tiles_n;  // ceil(N / kTn)
   int remap;
 };
@@ -71,9 +73,17 @@ void gemm_nt_kernel(const GemmParams p) {
   const int wm = wave & 1;   // 2 waves along m
   const int wn = wave >> 1;  // 4 waves along n
 
+  // Tile order: after the XCD remap each XCD runs consecutive tile ids; those ids go down
+  // groups of kGroupM tile rows first, so the 32 workgroups an XCD holds at a time share
+  // 8 A panels and 4 B panels in its L2 (one tile row would need 32 B panels).
   const int g = remap_block(blockIdx.x, p.remap);
-  const int tm = g / p.tiles_n;
-  const int tn = g - tm * p.tiles_n;
+  const int per_group = kGroupM * p.tiles_n;
+  const int group = g / per_group;
+  const int first_m = group * kGroupM;
+  const int rows_in_group = min(p.tiles_m - first_m, kGroupM);
+  const int local = g - group * per_group;
+  const int tm = first_m + local % rows_in_group;
+  const int tn = local / rows_in_group;
   const int m0 = tm * kTm, n0 = tn * kTn;
   const int K = p.K;
   const int nk = (K + kTk - 1) / kTk;
@@ -158,6 +168,7 @@ int gemm_bf16_nt(const void* a, const void* b, void* c, int M, int N, int K, voi
   p.M = M;
   p.N = N;
   p.K = K;
+  p.tiles_m = (int)tiles_m;
   p.tiles_n = (int)tiles_n;
   const int64_t grid = tiles_m * tiles_n;
   p.remap = (grid % 8 == 0) ? 1 : 0;
