@@ -53,9 +53,11 @@ extern "C" {
  *   stream   a hipStream_t passed as void*; NULL is the default stream.
  *
  * Ownership: the caller owns every buffer. The library allocates no device memory, keeps
- * no state between calls (apart from reading the tuning variable ATTN_FWD_BC once per
- * process: 32 or 64 keys per tile, default 64), and may be called concurrently from
- * several host threads on different streams.
+ * no state between calls, and may be called concurrently from several host threads on
+ * different streams. Each call reads two testing and tuning variables from the
+ * environment: ATTN_FWD_KERNEL=pingpong|fourwave overrides the kernel chosen by head
+ * dimension (ping-pong for D = 128, four-wave for D = 64; both give identical results),
+ * and ATTN_FWD_BC=32 selects 32-key tiles in the four-wave kernel (default 64).
  *
  * Behaviour: arguments are validated on the host before any HIP call; an invalid call
  * returns a negative code and enqueues nothing. A valid call enqueues one kernel and

@@ -10,8 +10,12 @@
 // those pages; they follow the usual FlashAttention conventions.
 //
 // gfx950 design (not the H100 one):
-//   * one workgroup = 4 waves; each wave owns 32 query rows, so a workgroup covers 128;
-//     two workgroups share a compute unit (two waves per SIMD).
+//   * each wave owns 32 query rows. Two kernels share the per-row arithmetic below and give
+//     identical results: at D = 128 the ping-pong kernel (8 waves, 256 queries per
+//     workgroup, one workgroup per compute unit, two wave groups alternating matrix and
+//     vector phases on every SIMD); at D = 64 the four-wave kernel (128 queries per
+//     workgroup, two workgroups per compute unit, each wave interleaving its own MFMAs and
+//     exponentials).
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: lane l
 //     then holds 16 keys of query (l % 32) per 32-key block, so the row max and row sum
 //     are in-lane reductions plus one v_permlane32_swap between the two lane halves.
@@ -19,11 +23,11 @@
 //     are already the B operand of that MFMA (8 keys of its query), given that the A
 //     operand (V^T) pairs its k positions with the same 8 keys; V^T fragments come from
 //     LDS through ds_read_b64_tr_b16, which transposes 4x16 bf16 blocks across lanes.
-//   * K and V tiles (64 keys by default, or 32) are copied global -> LDS by
-//     buffer_load ... lds into double-buffered rings; the K ring runs one tile ahead, so
-//     the score MFMAs of tile t+1 overlap the exponentials of tile t. The 16-byte chunks of
-//     each tile row are permuted so that the K reads and the transposing V reads are free
-//     of LDS bank conflicts.
+//   * K and V tiles (64 keys by default, or 32 in the four-wave kernel) are copied
+//     global -> LDS by buffer_load ... lds into double-buffered rings; the K ring runs one
+//     tile ahead, so the score MFMAs of tile t+1 overlap the exponentials of tile t. The
+//     16-byte chunks of each tile row are permuted so that the K reads and the transposing
+//     V reads are free of LDS bank conflicts.
 //   * the exp2 argument is fma(s, c, -m*c) with c = scale*log2(e) in fp32, on the fp32
 //     accumulator (the scale is never folded into bf16 Q). The running max only moves
 //     when a row's max grows by more than 2^8 (lazy rescaling), so O is rarely rescaled.
@@ -36,6 +40,7 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "attn_fwd.h"
 
@@ -52,6 +57,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kWaves = 4;
 constexpr int kQW = 32;              // query rows per wave
 constexpr int kBr = kWaves * kQW;    // query rows per workgroup
+constexpr int kWavesPP = 8;          // ping-pong kernel: waves per workgroup
+constexpr int kBrPP = kWavesPP * kQW;  // ping-pong kernel: query rows per workgroup
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr int kWaitVmcnt0 = 0x0F70;    // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
@@ -476,6 +483,321 @@ void attn_fwd_kernel(const Params p) {
   }
 }
 
+// ---- ping-pong kernel (the D = 128 path): one workgroup of 8 waves (two per SIMD, one
+// workgroup per compute unit) covers 256 queries. The waves form two groups (waves 0-3 and
+// 4-7; waves w and w + 4 share a SIMD) that run the same sequence of phases offset by one:
+// a matrix phase (P V of tile j - 1, then the scores of tile j: MFMAs and the LDS reads
+// feeding them) and a vector phase (mask, row max, lazy rescale and exponentials of tile
+// j). A workgroup barrier ends every phase, so on every SIMD one wave's MFMAs run while
+// the other wave's exponentials run; the matrix phase raises its wave's issue priority
+// (s_setprio) so that its MFMAs are never starved by the other wave's VALU stream. The
+// arithmetic per query row is that of attn_fwd_kernel, in the same order, so both kernels
+// give bit-identical results.
+
+// Instruction order of a full matrix phase: transposing V reads and K reads run two MFMAs
+// ahead of the MFMA that consumes them.
+template <int D, int BC>
+__device__ inline void matrix_phase_schedule() {
+  constexpr int kPvMfma = (BC / 16) * (D / 32);
+  constexpr int kQkMfma = (BC / 32) * (D / 16);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < kPvMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kQkMfma; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+template <int D, int BC, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_pp_kernel(const Params p) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  static_assert(BC == 64, "key tile");
+  constexpr int W = kWavesPP;
+  constexpr int kBc = BC;
+  constexpr int NB = BC / 32;
+  using L = TileLayout<D, BC, W>;
+  constexpr int RB = L::kRowBytes;
+  constexpr int kBrW = kBrPP;
+  __shared__ __attribute__((aligned(1024))) char smem[L::kLdsBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int col = lane & 31;
+  const int hi = lane >> 5;
+
+  int g = blockIdx.x;
+  if (p.remap) {
+    const int per_xcd = gridDim.x >> 3;
+    g = (g & 7) * per_xcd + (g >> 3);
+  }
+  const int bh = g / p.n_qtiles;
+  int qt = g - bh * p.n_qtiles;
+  if (CAUSAL) qt = p.n_qtiles - 1 - qt;
+  const int N = p.N;
+  const float c = p.c;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const __bf16* Qh = p.q + head;
+  const int q0 = qt * kBrW + wave * kQW;
+  const int qrow = q0 + col;
+  const bool wave_active = q0 < N;
+  const int wg_kv_end = CAUSAL ? min(N, (qt + 1) * kBrW) : N;
+  const int ntiles = (wg_kv_end + kBc - 1) / kBc;
+  const int T = !wave_active ? 0 : CAUSAL ? (min(N, q0 + kQW) + kBc - 1) / kBc : ntiles;
+
+  // K/V copies, shared by the 8 waves (the same layout and ragged-tile rule as
+  // attn_fwd_kernel)
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const i32x4 krsrc = make_rsrc(p.k + head, head_bytes);
+  const i32x4 vrsrc = make_rsrc(p.v + head, head_bytes);
+  uint32_t koff[L::kPeriodK], voff[L::kPeriodV];
+#pragma unroll
+  for (int i = 0; i < L::kPeriodK; ++i) {
+    const int row = (wave * L::kCopies + i) * L::kRowsPerCopy + lane / L::kChunks;
+    koff[i] = row * RB + (((lane % L::kChunks) ^ swz_k<D>(row)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < L::kPeriodV; ++i) {
+    const int row = (wave * L::kCopies + i) * L::kRowsPerCopy + lane / L::kChunks;
+    voff[i] = row * RB + (((lane % L::kChunks) ^ swz_v<D>(row)) << 4);
+  }
+  const uint32_t smem_lds = lds_address(smem);
+  auto copy_tile = [&](const i32x4& rsrc, const uint32_t* coff, int period, int t, uint32_t dst) {
+    const int key0 = t * kBc;
+    const uint32_t dst_w = dst + wave * L::kCopies * 1024;
+    if (key0 + kBc <= N) {
+#pragma unroll
+      for (int i = 0; i < L::kCopies; ++i) {
+        const uint32_t soff = __builtin_amdgcn_readfirstlane(key0 * RB + (i / period) * period * 1024);
+        copy16_to_lds(rsrc, coff[i % period], soff, dst_w + i * 1024);
+      }
+    } else {
+      const uint32_t last = (uint32_t)(N - key0 - 1);
+      const uint32_t soff = __builtin_amdgcn_readfirstlane(key0 * RB);
+#pragma unroll
+      for (int i = 0; i < L::kCopies; ++i) {
+        const uint32_t o = coff[i % period] + (i / period) * period * 1024;
+        copy16_to_lds(rsrc, (min(o / RB, last) * RB) | (o % RB), soff, dst_w + i * 1024);
+      }
+    }
+  };
+  const uint32_t kbuf_lds[2] = {smem_lds, smem_lds + L::kTileBytes};
+  const uint32_t vbuf_lds[2] = {smem_lds + 2 * L::kTileBytes, smem_lds + 3 * L::kTileBytes};
+  auto copy_k = [&](int t) { copy_tile(krsrc, koff, L::kPeriodK, t, kbuf_lds[t & 1]); };
+  auto copy_v = [&](int t) { copy_tile(vrsrc, voff, L::kPeriodV, t, vbuf_lds[t & 1]); };
+  copy_k(0);
+
+  bf16x8 qf[D / 16];
+  if (qrow < N) {
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D) + hi;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[s] = src[2 * s];
+  } else {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[s] = bf16x8{};
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  int k_addr[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) k_addr[st] = col * RB + 16 * ((2 * st + hi) ^ swz_k<D>(col));
+  const int jj = lane & 15;
+  const int gq = lane >> 4;
+  int v_addr[D / 32];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) {
+    const int row = 4 * hi + (jj >> 2);
+    const int chunk = 4 * d + 2 * (gq & 1) + ((jj >> 1) & 1);
+    v_addr[d] = row * RB + 16 * (chunk ^ swz_v<D>(row)) + 8 * (jj & 1);
+  }
+
+  float m = -INFINITY;
+  float l = 0.f;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) o[d] = f32x16{};
+  f32x16 s[NB];
+  bf16x8 pb[2 * NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) s[j] = f32x16{};
+#pragma unroll
+  for (int j = 0; j < 2 * NB; ++j) pb[j] = bf16x8{};
+
+  auto qk = [&](int t) {
+    const int kb = (t & 1) * L::kTileBytes;
+    // the NB accumulation chains alternate, so consecutive MFMAs are independent
+#pragma unroll
+    for (int j = 0; j < NB; ++j) s[j] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const char* a = smem + kb + k_addr[st] + 32 * j * RB;
+        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a), qf[st],
+                                                       s[j], 0, 0, 0);
+      }
+    }
+  };
+  auto pv = [&](int t) {
+    const int vb = 2 * L::kTileBytes + (t & 1) * L::kTileBytes;
+#pragma unroll
+    for (int st = 0; st < kBc / 16; ++st) {
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d) {
+        const char* a0 = smem + vb + v_addr[d] + 16 * st * RB;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a0);
+        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
+        const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[d], 0, 0, 0);
+      }
+    }
+  };
+  // vector phase of tile t: mask (a wave's last tile only), row max, lazy rescale,
+  // exponentials into pb and their sum into l
+  auto softmax = [&](int t, bool last) {
+    if (last) {
+      const int key0 = t * kBc;
+      if ((key0 + kBc > N) || (CAUSAL && key0 + kBc - 1 > q0)) {
+        const int limit = (CAUSAL ? min(N, qrow + 1) : N) - key0 - 4 * hi;
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * j + 8 * (r >> 2) + (r & 3) >= limit) s[j][r] = -INFINITY;
+      }
+    }
+    float mx = m;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
+    mx = max_across_halves(mx);
+    if (__builtin_amdgcn_ballot_w64((mx - m) * c > kRescaleLog2)) {
+      const float alpha = __builtin_amdgcn_exp2f((m - mx) * c);
+      m = mx;
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+    }
+    const float mc = m * c;
+    float rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][r], c, -mc));
+        rs += e;
+        pb[2 * j + (r >> 3)][r & 7] = (__bf16)e;
+      }
+    l += rs;
+  };
+
+  // Slot pairs i = 0 .. ntiles (two barriers each). The copies of K(i+1) and V(i) are
+  // issued at the start of pair i and waited for at its end; K(i+1) goes to the K slot
+  // that held K(i-1), last read in pair i-1, and V(i) to the V slot that held V(i-2), last
+  // read in pair i-1 too (two-slot rings). Group 0 runs, in pair i, the
+  // matrix phase of step i (P V of tile i-1, scores of tile i) and then the vector phase of
+  // tile i; group 1 runs the vector phase of tile i-1 and then the matrix phase of step i.
+  // Each group's sequence is straight-line code (first and last steps peeled), so the
+  // accumulators keep their registers across the loop.
+  auto copies = [&](int i) {
+    if (i + 1 < ntiles) copy_k(i + 1);
+    if (i < ntiles) copy_v(i);
+  };
+  auto matrix = [&](int i) {  // P V of tile i-1 and scores of tile i, both present
+    __builtin_amdgcn_s_setprio(2);
+    pv(i - 1);
+    qk(i);
+    matrix_phase_schedule<D, BC>();
+    __builtin_amdgcn_s_setprio(0);
+  };
+  wait_copies_and_barrier();
+  int i = 0;
+  if (T > 0) {
+    if (grp == 0) {
+      copies(0);
+      qk(0);
+      __syncthreads();
+      if (T == 1) {
+        softmax(0, true);
+      } else {
+        softmax(0, false);
+      }
+      wait_copies_and_barrier();
+      for (i = 1; i + 1 < T; ++i) {
+        copies(i);
+        matrix(i);
+        __syncthreads();
+        softmax(i, false);
+        wait_copies_and_barrier();
+      }
+      if (i < T) {  // i == T - 1 >= 1
+        copies(i);
+        matrix(i);
+        __syncthreads();
+        softmax(i, true);
+        wait_copies_and_barrier();
+        ++i;
+      }
+      copies(i);  // i == T
+      pv(T - 1);
+      __syncthreads();
+      wait_copies_and_barrier();
+      ++i;
+    } else {
+      copies(0);
+      __syncthreads();
+      qk(0);
+      wait_copies_and_barrier();
+      for (i = 1; i < T; ++i) {
+        copies(i);
+        softmax(i - 1, false);
+        __syncthreads();
+        matrix(i);
+        wait_copies_and_barrier();
+      }
+      copies(i);  // i == T
+      softmax(T - 1, true);
+      __syncthreads();
+      pv(T - 1);
+      wait_copies_and_barrier();
+      ++i;
+    }
+  }
+  for (; i <= ntiles; ++i) {
+    copies(i);
+    __syncthreads();
+    wait_copies_and_barrier();
+  }
+
+  if (wave_active) {
+    const float lt = sum_across_halves(l);
+    if (qrow < N) {
+      const float inv = 1.f / lt;
+      __bf16* orow = p.o + head + (size_t)qrow * D;
+#pragma unroll
+      for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          bf16x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = (__bf16)(o[d][4 * j4 + i] * inv);
+          *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * j4 + 4 * hi) = w;
+        }
+      if (hi == 0) p.lse[(size_t)bh * N + qrow] = (m * c + __builtin_log2f(lt)) * kLn2;
+    }
+  }
+}
+
 template <int D, int BC, int W>
 void launch(int causal, dim3 grid, hipStream_t s, const Params& p) {
   const dim3 block(64 * W);
@@ -483,16 +805,25 @@ void launch(int causal, dim3 grid, hipStream_t s, const Params& p) {
   else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, W, false>), grid, block, 0, s, p);
 }
 
-// Keys per K/V tile for head dimension D. ATTN_FWD_BC (32 or 64), read once, overrides
-// the default for tuning experiments.
-int key_tile(int D) {
-  static const int forced = [] {
-    const char* e = getenv("ATTN_FWD_BC");
-    const int v = e ? atoi(e) : 0;
-    return (v == 32 || v == 64) ? v : 0;
-  }();
-  if (forced) return forced;
-  return 64;
+// Kernel choice. D = 128 runs the ping-pong kernel; D = 64 runs the four-wave kernel: its
+// vector work per key tile is that of D = 128 while its matrix work halves, so the two
+// phases of a ping-pong pair would not balance (measured slower). Two environment
+// variables, read at every call so that tests can exercise each path in one process,
+// override the choice for testing and tuning: ATTN_FWD_KERNEL=pingpong|fourwave, and
+// ATTN_FWD_BC=32|64 for the key tile of the four-wave kernel.
+enum class Kernel { kPingPong, kFourWave };
+
+Kernel choose_kernel(int D) {
+  const char* e = getenv("ATTN_FWD_KERNEL");
+  if (e && strcmp(e, "pingpong") == 0) return Kernel::kPingPong;
+  if (e && strcmp(e, "fourwave") == 0) return Kernel::kFourWave;
+  return D == 128 ? Kernel::kPingPong : Kernel::kFourWave;
+}
+
+int key_tile() {
+  const char* e = getenv("ATTN_FWD_BC");
+  const int v = e ? atoi(e) : 0;
+  return (v == 32) ? 32 : 64;
 }
 
 }  // namespace
@@ -535,14 +866,29 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.c = scale * kLog2e;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid_dim((unsigned)grid);
-  const int bc = key_tile(D);
-  if (D == 64) {
-    if (bc == 32) launch<64, 32, kWaves>(causal, grid_dim, s, p);
-    else launch<64, 64, kWaves>(causal, grid_dim, s, p);
+  if (choose_kernel(D) == Kernel::kPingPong) {
+    const int64_t n_qtiles_pp = ((int64_t)N + kBrPP - 1) / kBrPP;
+    const int64_t grid_pp = (int64_t)B * H * n_qtiles_pp;
+    p.n_qtiles = (int)n_qtiles_pp;
+    p.remap = (grid_pp % 8 == 0) ? 1 : 0;
+    const dim3 gpp((unsigned)grid_pp), bpp(64 * kWavesPP);
+    if (D == 64) {
+      if (causal) hipLaunchKernelGGL((attn_fwd_pp_kernel<64, 64, true>), gpp, bpp, 0, s, p);
+      else hipLaunchKernelGGL((attn_fwd_pp_kernel<64, 64, false>), gpp, bpp, 0, s, p);
+    } else {
+      if (causal) hipLaunchKernelGGL((attn_fwd_pp_kernel<128, 64, true>), gpp, bpp, 0, s, p);
+      else hipLaunchKernelGGL((attn_fwd_pp_kernel<128, 64, false>), gpp, bpp, 0, s, p);
+    }
   } else {
-    if (bc == 32) launch<128, 32, kWaves>(causal, grid_dim, s, p);
-    else launch<128, 64, kWaves>(causal, grid_dim, s, p);
+    const dim3 grid_dim((unsigned)grid);
+    const int bc = key_tile();
+    if (D == 64) {
+      if (bc == 32) launch<64, 32, kWaves>(causal, grid_dim, s, p);
+      else launch<64, 64, kWaves>(causal, grid_dim, s, p);
+    } else {
+      if (bc == 32) launch<128, 32, kWaves>(causal, grid_dim, s, p);
+      else launch<128, 64, kWaves>(causal, grid_dim, s, p);
+    }
   }
   if (hipGetLastError() != hipSuccess) return ATTN_FWD_ELAUNCH;
   return ATTN_FWD_OK;
