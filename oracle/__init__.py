@@ -11,9 +11,11 @@ code. Modules:
   backward   the gradients dQ, dK, dV of the forward definition, by the chain rule
   decode     few queries against a long key/value sequence (bottom-right causal mask)
   gemm       the plain matrix product C = A B^T
+  based      Based linear attention (second-order Taylor feature map), causal
 
 Every function here is pinned by ``tests/test_oracle.py``, ``tests/test_oracle_bwd.py``,
-``tests/test_oracle_decode.py`` and ``tests/test_oracle_gemm.py``
+``tests/test_oracle_decode.py``, ``tests/test_oracle_gemm.py`` and
+``tests/test_oracle_based.py``
 against closed forms, invariants, a hand-derived worked example, brute force and finite
 differences.
 """
@@ -21,6 +23,7 @@ from .attention import attention_fwd, attention_head, attention_probs, attention
 from .backward import attention_bwd, attention_bwd_head
 from .decode import attention_decode
 from .gemm import gemm_nt
+from .based import based_linear_attention, based_recurrent
 from .brute import attention_brute
 from .online import attention_online
 
@@ -35,4 +38,6 @@ __all__ = [
     "attention_bwd_head",
     "attention_decode",
     "gemm_nt",
+    "based_linear_attention",
+    "based_recurrent",
 ]
