@@ -1,12 +1,13 @@
 """MI355X-native fused softmax attention (gfx950 HIP kernels behind a C ABI).
 
-``attn_fwd``, ``attn_bwd``, ``attn_decode`` and ``gemm_nt`` are thin Python bindings over ``libattn_fwd.so``; the
+``attn_fwd``, ``attn_bwd``, ``attn_decode``, ``gemm_nt`` and ``based_fwd`` are thin Python bindings over
+``libattn_fwd.so``; the
 library is loaded on first use and its absence is an error (there is no fallback path).
 """
-from .binding import (AttnBwdError, AttnDecodeError, AttnFwdError, GemmError, attn_bwd,
-                      attn_decode, attn_fwd, bwd_workspace_bytes, decode_workspace_bytes, gemm_nt,
-                      library_path, load_library)
+from .binding import (AttnBwdError, AttnDecodeError, AttnFwdError, BasedFwdError, GemmError,
+                      attn_bwd, attn_decode, attn_fwd, based_fwd, bwd_workspace_bytes,
+                      decode_workspace_bytes, gemm_nt, library_path, load_library)
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "gemm_nt", "bwd_workspace_bytes",
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "gemm_nt", "based_fwd", "bwd_workspace_bytes",
            "decode_workspace_bytes", "library_path", "load_library", "AttnFwdError", "AttnBwdError",
-           "AttnDecodeError", "GemmError"]
+           "AttnDecodeError", "GemmError", "BasedFwdError"]

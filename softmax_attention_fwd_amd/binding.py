@@ -89,6 +89,10 @@ def load_library():
         lib.gemm_bf16_nt.restype = ci
         lib.gemm_strerror.argtypes = [ci]
         lib.gemm_strerror.restype = ctypes.c_char_p
+        lib.based_fwd.argtypes = [vp] * 4 + [ci] * 5 + [vp]
+        lib.based_fwd.restype = ci
+        lib.based_fwd_strerror.argtypes = [ci]
+        lib.based_fwd_strerror.restype = ctypes.c_char_p
         _lib = lib
         return lib
 
@@ -326,4 +330,47 @@ def gemm_nt(a, b, out=None, stream=None):
         if code in (ATTN_FWD_EINVAL, ATTN_FWD_EALIGN):
             raise ValueError(f"gemm_bf16_nt rejected its arguments (code {code}): {msg}")
         raise GemmError(code, msg)
+    return out
+
+
+BASED_D = 16
+BASED_DV = 64
+
+
+class BasedFwdError(RuntimeError):
+    """A nonzero return code from based_fwd."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"based_fwd failed with code {code}: {message}")
+        self.code = code
+
+
+def based_fwd(q, k, v, out=None, stream=None):
+    """Based linear attention (causal) on the GPU: q, k [B, H, N, 16] and v [B, H, N, 64],
+    contiguous bfloat16 CUDA tensors on one device. Returns o bfloat16 [B, H, N, 64]
+    (``out`` to write in place)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(name, t)
+    if q.shape != k.shape or v.shape[:3] != q.shape[:3] or q.device != k.device or q.device != v.device:
+        raise ValueError(f"q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}: expected q, k "
+                         "[B,H,N,d] and v [B,H,N,dv] on one device")
+    B, H, N, d = (int(x) for x in q.shape)
+    dv = int(v.shape[3])
+    if d != BASED_D or dv != BASED_DV:
+        raise ValueError(f"based_fwd needs d = {BASED_D} and dv = {BASED_DV}, got {d} and {dv}")
+    if out is None:
+        out = torch.empty((B, H, N, dv), dtype=torch.bfloat16, device=q.device)
+    elif (tuple(out.shape) != (B, H, N, dv) or out.dtype != torch.bfloat16 or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError("out must be a contiguous bfloat16 [B, H, N, 64] tensor on q's device")
+    lib = load_library()
+    code = lib.based_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d, dv,
+                         _stream_handle(stream, q.device))
+    if code != ATTN_FWD_OK:
+        msg = lib.based_fwd_strerror(code).decode()
+        if code in (ATTN_FWD_EINVAL, ATTN_FWD_EUNSUPPORTED, ATTN_FWD_EALIGN):
+            raise ValueError(f"based_fwd rejected its arguments (code {code}): {msg}")
+        raise BasedFwdError(code, msg)
     return out

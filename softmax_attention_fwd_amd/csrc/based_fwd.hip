@@ -1,0 +1,417 @@
+// Based linear attention forward (causal) for gfx950 (AMD Instinct MI355X, CDNA4).
+//
+// What is computed: for every (batch, head) and token i, with d = 16 query/key features
+// and dv = 64 value features,
+//   s_ij = q_i . k_j / 4,   w_ij = 1 + s_ij + s_ij^2 / 2  (j <= i),
+//   o_i  = sum_j w_ij v_j / sum_j w_ij.
+// The pages ("ThunderKittens 2.0: Faster Kernels, Talking Models, and More Adorable
+// Kittens", thebeat.tech, sections "New Kernels for Enhanced Performance" and "Performance
+// Benchmarks") name Based linear attention without its formulas; this is the published
+// Based design: the second-order Taylor feature map of exp(q.k / sqrt(d)),
+//   phi(x) = [1, x / 2, vec(x x^T) / (4 sqrt 2)],   phi(q) . phi(k) = w,
+// so that o_i = phi(q_i)^T S / phi(q_i)^T z with running sums S = sum phi(k_j) v_j^T
+// (273 x 64) and z = sum phi(k_j).
+//
+// gfx950 design: one workgroup of 4 waves per (batch, head) walks the sequence in chunks
+// of 64 tokens. The state S lives in MFMA accumulators (fp32) spread over the 4 waves:
+// wave w owns the 64 quadratic features with first index a in [4w, 4w + 4) for all 64
+// value columns, plus the linear and constant features for value columns [16w, 16w + 16).
+// For chunk c the waves split the 64 tokens (16 each) and compute
+//   * O_inter^T = S^T phi(Q_c)^T from a bf16 copy of S^T in LDS (written after chunk c-1),
+//   * O_intra^T = V_c^T W^T with W the causal Taylor weights inside the chunk,
+//   * the normaliser: t0 + q . ksum / 4 + q^T KK q / 32 in fp32, with KK = sum k k^T and
+//     ksum = sum k over earlier chunks (KK enters an MFMA as a bf16 hi + lo pair),
+//     plus the row sums of W,
+// then update their part of S with phi(K_c)^T V_c and publish the new bf16 S^T for the
+// next chunk. All products are v_mfma_f32_16x16x32_bf16. The quadratic features of K
+// are formed in registers: each lane holds k[token][b] for 8 tokens (transposing LDS
+// reads) and receives k[token][a] from lane a of its 16-lane row (DPP row broadcast).
+// Chunk c+1's Q, K, V are copied global -> LDS (buffer_load ... lds) during chunk c;
+// rows past N read as zeros, so they add nothing to S, KK and ksum.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "based_fwd.h"
+#include "tile_lds.h"
+
+namespace {
+
+using namespace attn_tile;
+
+constexpr int kD = 16;        // query/key features
+constexpr int kDv = 64;       // value features
+constexpr int kChunk = 64;    // tokens per chunk
+constexpr int kWaves = 4;
+constexpr int kStRow = 296;   // bf16 per S^T row in LDS: 288 features + 8 (592-byte rows keep
+                              // the 16-byte reads of 16 consecutive rows bank-conflict free)
+constexpr float kC2 = 0.17677669529663688f;  // 1 / (4 sqrt 2), the quadratic feature scale
+
+// LDS layout (bytes): two stages of {Q, K, V} chunk tiles, two S^T buffers, two
+// {KK hi, KK lo} buffers, two ksum buffers.
+constexpr int kQBytes = kChunk * kD * 2;
+constexpr int kVBytes = kChunk * kDv * 2;
+constexpr int kStage = 2 * kQBytes + kVBytes;
+constexpr int kStBytes = kDv * kStRow * 2;
+constexpr int kKKBytes = 2 * kD * kD * 2;
+constexpr int kOffSt = 2 * kStage;
+constexpr int kOffKK = kOffSt + 2 * kStBytes;
+constexpr int kOffKs = kOffKK + 2 * kKKBytes;
+constexpr int kLds = kOffKs + 2 * kD * 4;
+
+struct BasedParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  int N;
+  int n_chunks;
+};
+
+// V chunk tiles (128-byte rows) keep their 16-byte chunks permuted: logical chunk j of row r
+// at j ^ swz_v(r). A transposing read covers, per 32 lanes, 8 consecutive rows and two
+// adjacent chunks; with this permutation those 8 rows land on 8 distinct bank ranges.
+__device__ inline int swz_v(int r) { return ((r >> 1) & 3) << 1; }
+
+__device__ inline float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ inline float bf_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+
+__device__ inline bf16x8 pack8(const float (&x)[8]) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (__bf16)x[j];
+  return r;
+}
+
+// DPP row_newbcast:n: every lane of a 16-lane row receives x from lane n of that row.
+template <int n>
+__device__ inline uint32_t row_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + n, 0xf, 0xf, false);
+}
+template <int W>
+__device__ inline uint32_t row_bcast_feature(uint32_t x, int rb) {
+  switch (rb) {  // rb is a compile-time constant after unrolling
+    case 0: return row_bcast<4 * W + 0>(x);
+    case 1: return row_bcast<4 * W + 1>(x);
+    case 2: return row_bcast<4 * W + 2>(x);
+    default: return row_bcast<4 * W + 3>(x);
+  }
+}
+
+__device__ inline float sum_across_16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposing read of a 4-row x 16-column bf16 block: in every 16-lane row, lane c supplies
+// the address of row (c >> 2), columns 4 (c & 3) .. + 3 and receives column c of the 4 rows.
+__device__ inline bf16x4 tr4(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+}
+
+// One wave's share of copying chunk `chunk` (rows past N read zeros: their offsets are
+// placed outside the buffer range on purpose). Copies 0-1: Q, 2-3: K (32 rows of 32 bytes
+// each), 4-11: V (8 rows of 128 bytes each, chunk-permuted); wave w issues 3w .. 3w + 2.
+__device__ inline void copy_chunk(const i32x4& qr, const i32x4& kr, const i32x4& vr, int chunk, int N,
+                                  uint32_t stage_lds, int w, int lane) {
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int i = 3 * w + u;
+    const int t0 = chunk * kChunk;
+    if (i < 4) {
+      const int row = 32 * (i & 1) + (lane >> 1);
+      const uint32_t voff = (t0 + row < N) ? (uint32_t)((t0 + row) * 32 + 16 * (lane & 1)) : 0x80000000u;
+      const uint32_t dst = stage_lds + (i < 2 ? 0 : kQBytes) + 1024 * (i & 1);
+      copy16_to_lds(i < 2 ? qr : kr, voff, 0, __builtin_amdgcn_readfirstlane(dst));
+    } else {
+      const int row = 8 * (i - 4) + (lane >> 3);
+      const int logical = (lane & 7) ^ swz_v(row);
+      const uint32_t voff = (t0 + row < N) ? (uint32_t)((t0 + row) * 128 + 16 * logical) : 0x80000000u;
+      const uint32_t dst = stage_lds + 2 * kQBytes + 1024 * (i - 4);
+      copy16_to_lds(vr, voff, 0, __builtin_amdgcn_readfirstlane(dst));
+    }
+  }
+}
+
+// The chunk loop of wave W (its features and tokens are compile-time).
+template <int W>
+__device__ inline void based_wave(const BasedParams& p, char* smem, int lane) {
+  const int g = lane >> 4;  // 16-lane row
+  const int c = lane & 15;  // lane within the row
+  const int N = p.N;
+  const size_t bh = blockIdx.x;
+  const i32x4 qr = make_rsrc(p.q + bh * N * kD, (uint32_t)N * kD * 2);
+  const i32x4 kr = make_rsrc(p.k + bh * N * kD, (uint32_t)N * kD * 2);
+  const i32x4 vr = make_rsrc(p.v + bh * N * kDv, (uint32_t)N * kDv * 2);
+  __bf16* ob = p.o + bh * N * kDv;
+  const uint32_t smem_lds = lds_address(smem);
+
+  // S^T buffer 0, KK buffer 0 and ksum buffer 0 start at zero
+  for (int i = W * 64 + lane; i < kStBytes / 4; i += kWaves * 64) reinterpret_cast<uint32_t*>(smem + kOffSt)[i] = 0u;
+  for (int i = W * 64 + lane; i < kKKBytes / 4; i += kWaves * 64) reinterpret_cast<uint32_t*>(smem + kOffKK)[i] = 0u;
+  if (W == 0 && lane < kD) reinterpret_cast<float*>(smem + kOffKs)[lane] = 0.f;
+  copy_chunk(qr, kr, vr, 0, N, smem_lds, W, lane);
+
+  f32x4 sq[4][4];  // quadratic features (a = 4W + rb, b = 4g + i) x value columns 16cb + c
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) sq[rb][cb] = f32x4{};
+  f32x4 slin = {};   // linear features b = 4g + i (value / 2) x value columns 16W + c
+  f32x4 sconst = {}; // row 0: sum of v over value columns 16W + c; rows 1-15 stay zero
+  f32x4 kk = {};     // wave 0: KK[a = 4g + i][b = c]
+  float ksum_part = 0.f;  // wave 0: sum of k[token][c] over this lane's tokens
+
+  wait_copies_and_barrier();
+  for (int t = 0; t < p.n_chunks; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < p.n_chunks) copy_chunk(qr, kr, vr, t + 1, N, smem_lds + (cur ^ 1) * kStage, W, lane);
+    const char* Qs = smem + cur * kStage;
+    const char* Ks = Qs + kQBytes;
+    const char* Vs = Ks + kQBytes;
+    const char* St = smem + kOffSt + cur * kStBytes;
+    const char* KKs = smem + kOffKK + cur * kKKBytes;
+    const float* kss = reinterpret_cast<const float*>(smem + kOffKs) + cur * kD;
+
+    // ---- this lane's query token (16W + c) and its features
+    const int tq = 16 * W + c;
+    // feature f = 32 ks + 8 g + j = 16 a + b: a = 2 ks + (g >> 1), b = 8 (g & 1) + j. qb holds
+    // q[tq][8 (g & 1) + j] (one lane-addressed read); qa[m] = q[tq][2 m + (g >> 1)] is the
+    // low or high bf16 of the m-th dword of the row, taken with a per-lane shift (a select
+    // here would be turned into per-lane register indexing).
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 qrow = *reinterpret_cast<const u32x4*>(Qs + tq * 32);
+    const u32x4 qrow1 = *reinterpret_cast<const u32x4*>(Qs + tq * 32 + 16);
+    const bf16x8 qbv = *reinterpret_cast<const bf16x8*>(Qs + tq * 32 + 16 * (g & 1));
+    const uint32_t sh = (g >> 1) ? 0u : 16u;
+    float qa[8], qb[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      qa[m] = __uint_as_float((qrow[m] << sh) & 0xFFFF0000u);
+      qa[4 + m] = __uint_as_float((qrow1[m] << sh) & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qb[j] = (float)qbv[j];
+    const bf16x8 bq_plain = g < 2 ? qbv : bf16x8{};  // q[tq][8g + j] for g < 2, else 0
+
+    // ---- O_inter^T = S^T phi(Q)^T over the 288 (padded) features, 9 steps of 32
+    f32x4 o[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) o[cb] = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) {
+      float f[8];
+      if (ks < 8) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = qa[ks] * (qb[j] * kC2);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = g < 2 ? 0.5f * qb[j] : ((g == 2 && j == 0) ? 1.f : 0.f);
+      }
+      const bf16x8 bfeat = pack8(f);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(St + (16 * cb + c) * (kStRow * 2) + 2 * (32 * ks + 8 * g));
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfeat, o[cb], 0, 0, 0);
+      }
+    }
+
+    // ---- V^T fragments of the chunk: tokens 32 m + 4 g + j (j < 4) and 32 m + 16 + 4 g + j - 4
+    bf16x8 vf[2][4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int r = 32 * m + 4 * g + (c >> 2);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int chunk = (2 * cb + ((c & 3) >> 1)) ^ swz_v(r);
+        const char* a0 = Vs + r * 128 + 16 * chunk + 8 * (c & 1);
+        vf[m][cb] = __builtin_shufflevector(tr4(a0), tr4(a0 + 16 * 128), 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
+
+    // ---- intra-chunk: W^T for keys 16 kb + 4 g + i (kb <= W) against token tq
+    float zpart = 0.f;
+    float wv[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if (kb <= W) {
+        const bf16x8 ak = g < 2 ? *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + c) * 32 + 16 * g) : bf16x8{};
+        const f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bq_plain, f32x4{}, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = 0.25f * s[i];
+          const float wt = 1.f + x + 0.5f * x * x;
+          wv[kb][i] = (kb < W || 4 * g + i <= c) ? wt : 0.f;
+          zpart += wv[kb][i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[kb][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m <= (W >> 1); ++m) {
+      bf16x8 bw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bw[i] = (__bf16)wv[2 * m][i];
+        bw[4 + i] = (__bf16)wv[2 * m + 1][i];
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[m][cb], bw, o[cb], 0, 0, 0);
+    }
+
+    // ---- normaliser: t0 + q . ksum / 4 + q^T KK q / 32 (earlier chunks) + row sum of W
+    {
+      const bf16x8 khi = g < 2 ? *reinterpret_cast<const bf16x8*>(KKs + c * 32 + 16 * g) : bf16x8{};
+      const bf16x8 klo = g < 2 ? *reinterpret_cast<const bf16x8*>(KKs + 512 + c * 32 + 16 * g) : bf16x8{};
+      f32x4 u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, bq_plain, f32x4{}, 0, 0, 0);
+      u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(klo, bq_plain, u, 0, 0, 0);  // u[i] = (KK q)[4g + i]
+      const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qs + tq * 32 + 8 * g);
+      const f32x4 ks4 = *reinterpret_cast<const f32x4*>(kss + 4 * g);
+      float zq = 0.f, zl = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        zq += (float)q4[i] * u[i];
+        zl += (float)q4[i] * ks4[i];
+      }
+      zpart += zq * (1.f / 32.f) + zl * 0.25f;
+    }
+    const float z = (float)(t * kChunk) + sum_across_halves(sum_across_16(zpart));
+
+    // ---- output rows: lane holds o^T[16 cb + 4 g + i][tq]
+    const int token = t * kChunk + tq;
+    if (token < N) {
+      const float inv = 1.f / z;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        bf16x4 wo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wo[i] = (__bf16)(o[cb][i] * inv);
+        *reinterpret_cast<bf16x4*>(ob + (size_t)token * kDv + 16 * cb + 4 * g) = wo;
+      }
+    }
+
+    // ---- state update with this chunk: S += phi(K)^T V, KK += K^T K, ksum += sum k
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const char* k0 = Ks + (32 * m + 4 * g + (c >> 2)) * 32 + 8 * (c & 3);
+      const bf16x8 kc = __builtin_shufflevector(tr4(k0), tr4(k0 + 16 * 32), 0, 1, 2, 3, 4, 5, 6, 7);
+      float kf[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kf[j] = (float)kc[j];  // k[token_j][c]
+      const u32x4 kd = __builtin_bit_cast(u32x4, kc);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        float f[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t ka = row_bcast_feature<W>(kd[d], rb);  // k[token][4W + rb]
+          f[2 * d] = bf_lo(ka) * (kf[2 * d] * kC2);
+          f[2 * d + 1] = bf_hi(ka) * (kf[2 * d + 1] * kC2);
+        }
+        const bf16x8 afeat = pack8(f);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          sq[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afeat, vf[m][cb], sq[rb][cb], 0, 0, 0);
+      }
+      float fl[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fl[j] = 0.5f * kf[j];
+      slin = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(fl), vf[m][W], slin, 0, 0, 0);
+      bf16x8 ones;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ones[j] = (__bf16)(c == 0 ? 1.f : 0.f);
+      sconst = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, vf[m][W], sconst, 0, 0, 0);
+      if (W == 0) {
+        kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, kc, kk, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ksum_part += kf[j];
+      }
+    }
+
+    // ---- publish the state after this chunk for the next one
+    char* Stn = smem + kOffSt + (cur ^ 1) * kStBytes;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        bf16x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = (__bf16)sq[rb][cb][i];
+        *reinterpret_cast<bf16x4*>(Stn + (16 * cb + c) * (kStRow * 2) + 2 * (16 * (4 * W + rb) + 4 * g)) = x;
+      }
+    {
+      bf16x4 xl, xc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xl[i] = (__bf16)slin[i];
+        xc[i] = (__bf16)sconst[i];
+      }
+      *reinterpret_cast<bf16x4*>(Stn + (16 * W + c) * (kStRow * 2) + 2 * (256 + 4 * g)) = xl;
+      *reinterpret_cast<bf16x4*>(Stn + (16 * W + c) * (kStRow * 2) + 2 * (272 + 4 * g)) = xc;
+    }
+    if (W == 0) {
+      __bf16* KKn = reinterpret_cast<__bf16*>(smem + kOffKK + (cur ^ 1) * kKKBytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 hi = (__bf16)kk[i];
+        KKn[(4 * g + i) * kD + c] = hi;
+        KKn[256 + (4 * g + i) * kD + c] = (__bf16)(kk[i] - (float)hi);
+      }
+      const float ks = sum_across_halves(sum_across_16(ksum_part));
+      if (g == 0) reinterpret_cast<float*>(smem + kOffKs)[(cur ^ 1) * kD + c] = ks;
+    }
+    wait_copies_and_barrier();
+  }
+}
+
+__global__ __launch_bounds__(256) void based_fwd_kernel(const BasedParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLds];
+  const int lane = threadIdx.x & 63;
+  switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+    case 0: based_wave<0>(p, smem, lane); break;
+    case 1: based_wave<1>(p, smem, lane); break;
+    case 2: based_wave<2>(p, smem, lane); break;
+    default: based_wave<3>(p, smem, lane); break;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int based_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+              int dv, void* stream) {
+  if (!q || !k || !v || !o) return BASED_EINVAL;
+  if (B < 1 || H < 1 || N < 1) return BASED_EINVAL;
+  if (d != kD || dv != kDv) return BASED_EUNSUPPORTED;
+  if ((int64_t)N * kDv * 2 >= ((int64_t)1 << 31) || (int64_t)B * H >= ((int64_t)1 << 31)) return BASED_EINVAL;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) != 0) return BASED_EALIGN;
+  BasedParams p;
+  p.q = static_cast<const __bf16*>(q);
+  p.k = static_cast<const __bf16*>(k);
+  p.v = static_cast<const __bf16*>(v);
+  p.o = static_cast<__bf16*>(o);
+  p.N = N;
+  p.n_chunks = (N + kChunk - 1) / kChunk;
+  hipLaunchKernelGGL(based_fwd_kernel, dim3((unsigned)(B * H)), dim3(64 * kWaves), 0,
+                     static_cast<hipStream_t>(stream), p);
+  if (hipGetLastError() != hipSuccess) return BASED_ELAUNCH;
+  return BASED_OK;
+}
+
+const char* based_fwd_strerror(int code) {
+  switch (code) {
+    case BASED_OK: return "success";
+    case BASED_EINVAL: return "invalid argument (NULL pointer, size < 1, or size overflow)";
+    case BASED_EUNSUPPORTED: return "unsupported feature sizes (d must be 16 and dv 64)";
+    case BASED_EALIGN: return "misaligned pointer (q, k, v, o need 16 bytes)";
+    case BASED_ELAUNCH: return "kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

@@ -153,3 +153,54 @@ def decode_inputs(w: DecodeWorkload):
             x.mul_(sigma)
         out.append(x.to(torch.bfloat16).contiguous())
     return tuple(out)
+
+
+@dataclass(frozen=True)
+class BasedWorkload:
+    """A Based linear-attention problem: q, k [B, H, N, d], v [B, H, N, dv], causal."""
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int = 16
+    dv: int = 64
+    seed: int = 0
+
+    @property
+    def hbm_bytes(self) -> int:
+        """Algorithmic HBM bytes: q, k, v read once and o written once, all bf16."""
+        return 2 * self.B * self.H * self.N * (2 * self.d + 2 * self.dv)
+
+    @property
+    def flops(self) -> int:
+        """Algorithmic flop of the chunked linear-time form with 64-token chunks: per token
+        2 * 273 * dv for the state update and 2 * 273 * dv for the inter-chunk product, and
+        per chunk pair (query, key) inside the chunk (64 * 65 / 2 of them) 2 * (d + dv)."""
+        F = 1 + self.d + self.d * self.d
+        n_chunks = -(-self.N // 64)
+        intra = n_chunks * (64 * 65 // 2) * 2 * (self.d + self.dv)
+        return self.B * self.H * (4 * F * self.dv * self.N + intra)
+
+    def describe(self) -> str:
+        return f"B{self.B} H{self.H} N{self.N} d{self.d} dv{self.dv} causal"
+
+
+# Based shapes: the published design's 16 query/key features and 64-wide heads, on the
+# batch, heads and length of the attention forward's workload 3, and a longer sequence.
+BASED_WORKLOADS = {
+    1: BasedWorkload("b1_b2h4n1024", 2, 4, 1024, seed=3001),
+    2: BasedWorkload("b2_b16h16n4096", 16, 16, 4096, seed=3002),
+    3: BasedWorkload("b3_b4h16n16384", 4, 16, 16384, seed=3003),
+}
+
+
+def based_inputs(w: BasedWorkload):
+    """q, k [B, H, N, d] and v [B, H, N, dv] (CPU bfloat16): one generator seeded with
+    w.seed draws q, then k, then v as standard normals, rounded to bfloat16."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(w.seed))
+    out = []
+    for dim in (w.d, w.d, w.dv):
+        out.append(torch.randn((w.B, w.H, w.N, dim), generator=g, dtype=torch.float32)
+                   .to(torch.bfloat16).contiguous())
+    return tuple(out)

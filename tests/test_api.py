@@ -48,13 +48,16 @@ def test_header_declares_entry_points():
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "tile_gemm.h")).read(), flags=re.S)
     assert sorted(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(gemm_\w+)\s*\(", text, flags=re.M)) == \
         ["gemm_bf16_nt", "gemm_strerror"]
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "based_fwd.h")).read(), flags=re.S)
+    assert sorted(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(based_\w+)\s*\(", text, flags=re.M)) == \
+        ["based_fwd", "based_fwd_strerror"]
 
 
 def test_exports_every_declared_symbol(lib):
     import subprocess
     exported = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
                               capture_output=True, text=True, check=True).stdout.split()
-    for name in declared_functions() + ["gemm_bf16_nt", "gemm_strerror"]:
+    for name in declared_functions() + ["gemm_bf16_nt", "gemm_strerror", "based_fwd", "based_fwd_strerror"]:
         assert hasattr(lib, name), f"{name} declared in include/ but not exported"
         assert name in exported
 
@@ -226,3 +229,38 @@ def test_gemm_codes_and_strerror(lib):
 ])
 def test_gemm_invalid_arguments_rejected(lib, args, code):
     assert lib.gemm_bf16_nt(*args, None) == code
+
+
+def test_based_codes_and_strerror(lib):
+    text = open(os.path.join(ROOT, "include", "based_fwd.h")).read()
+    codes = {n: int(v) for n, v in re.findall(r"#define\s+(BASED_\w+)\s+(-?\d+)", text)}
+    assert codes == {"BASED_OK": 0, "BASED_EINVAL": -1, "BASED_EUNSUPPORTED": -2, "BASED_EALIGN": -3,
+                     "BASED_ELAUNCH": -4}
+    msgs = {lib.based_fwd_strerror(c).decode() for c in codes.values()}
+    assert len(msgs) == len(codes) and "unknown error code" not in msgs
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, A, A, A, 1, 1, 64, 16, 64), -1), ((A, None, A, A, 1, 1, 64, 16, 64), -1),
+    ((A, A, None, A, 1, 1, 64, 16, 64), -1), ((A, A, A, None, 1, 1, 64, 16, 64), -1),
+    ((A, A, A, A, 0, 1, 64, 16, 64), -1), ((A, A, A, A, 1, 0, 64, 16, 64), -1),
+    ((A, A, A, A, 1, 1, 0, 16, 64), -1), ((A, A, A, A, 1, 1, 1 << 24, 16, 64), -1),
+    ((A, A, A, A, 1, 1, 64, 32, 64), -2), ((A, A, A, A, 1, 1, 64, 16, 128), -2),
+    ((A + 8, A, A, A, 1, 1, 64, 16, 64), -3), ((A, A, A + 2, A, 1, 1, 64, 16, 64), -3),
+    ((A, A, A, A + 4, 1, 1, 64, 16, 64), -3),
+])
+def test_based_invalid_arguments_rejected(lib, args, code):
+    assert lib.based_fwd(*args, None) == code
+
+
+def test_based_binding_rejects_cpu_and_bad_shapes():
+    import torch
+    from softmax_attention_fwd_amd import based_fwd
+    q = torch.zeros(1, 1, 8, 16, dtype=torch.bfloat16)
+    v = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        based_fwd(q, q, v)
+    with pytest.raises(ValueError, match="bfloat16"):
+        based_fwd(q.float(), q, v)
+    with pytest.raises(TypeError):
+        based_fwd(q.numpy(), q, v)
