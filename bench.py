@@ -1,14 +1,17 @@
 #!/usr/bin/env python3
 """Attention forward throughput on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload 3] [--gpus 1] [--op fwd|bwd|decode]
+    python bench.py [--steps K] [--warmup W] [--workload 3] [--gpus 1]
+                    [--op fwd|bwd|decode|gemm|based]
 
 One step = one attn_fwd call (the whole fused forward: K/V streaming, both contractions,
 online softmax, epilogue) over the workload's full tensors, already resident in HBM; with
 --op bwd, one attn_bwd call (its kernels: Delta, dK/dV, dQ) on the same shapes; with
 --op decode, one attn_decode call (split kernel + merge) on a decode workload (1..3:
 few queries against a long KV cache), reported in GB/s of K and V read against HBM; with
---op gemm, one C = A B^T (bf16) of --gemm-shape M,N,K, in TFLOP/s (2*M*N*K).
+--op gemm, one C = A B^T (bf16) of --gemm-shape M,N,K, in TFLOP/s (2*M*N*K); with
+--op based, one based_fwd call (Based linear attention, causal, d = 16, dv = 64) on a
+Based workload (1..3, default 2: B16 H16 N4096), in GB/s of q, k, v, o against HBM.
 The default workload is B16 H16 N4096 D128 non-causal with bf16 inputs. Prints ONE JSON
 line on stdout; details go to stderr.
 
@@ -319,16 +322,91 @@ def run_gemm(args) -> int:
     return 0
 
 
+def run_based(args) -> int:
+    import torch
+
+    from softmax_attention_fwd_amd import based_fwd
+    from softmax_attention_fwd_amd.inputs import BASED_WORKLOADS, based_inputs
+
+    w = BASED_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"[bench] based workload: {w.describe()}; generating inputs (seed {w.seed})")
+    q, k, v = based_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(vd)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        based_fwd(qd, kd, vd, out=o, stream=stream)
+
+    total_ms, launch_ms, wall = time_steps(step, stream, args.steps, args.warmup)
+    mean_launch = statistics.fmean(launch_ms)
+    value = w.hbm_bytes * args.steps / (total_ms * 1e-3) / 1e9
+    achieved = w.hbm_bytes / (mean_launch * 1e-3) / 1e9
+    tflops = w.flops / (mean_launch * 1e-3) / 1e12
+    log(f"[bench] span {total_ms:.3f} ms for {args.steps} steps; launch median "
+        f"{statistics.median(launch_ms):.4f} ms; {achieved:.1f} GB/s = "
+        f"{100 * achieved / PEAK_HBM_GBS:.1f}% of HBM peak; {tflops:.1f} TFLOP/s of the chunked form")
+    result = {
+        "metric": "Based linear attention fwd (causal) GB/s of q, k, v, o against HBM peak",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(total_ms / args.steps, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q, k, v)",
+        "config": {"workload": w.name, "op": "based", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "dv": w.dv, "causal": True, "parallelism": "single GPU"},
+        "launch_ms": {"mean": round(mean_launch, 5), "median": round(statistics.median(launch_ms), 5),
+                      "min": round(min(launch_ms), 5), "max": round(max(launch_ms), 5)},
+        "tflops_chunked_form": round(tflops, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "traffic_algorithmic": w.hbm_bytes},
+        "cpu_baseline": None,
+    }
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: 3 x 512 MiB device-to-device")
+        del src, dst
+    if not args.no_cpu_baseline:
+        import numpy as np
+
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        per_head = w.hbm_bytes / (w.B * w.H)
+        qn, kn, vn = (t.double().numpy() for t in (q, k, v))
+        done, t0 = 0, time.perf_counter()
+        while True:
+            b, h = divmod(done % (w.B * w.H), w.H)
+            oracle.based_linear_attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1])
+            done += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": round(done * per_head / dt / 1e9, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} heads of {w.describe()} by the quadratic definition (fp64 numpy, BLAS "
+                      f"threads as numpy sets them) in {dt:.1f} s"}
+        log(f"[bench] cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=40,
                     help="untimed launches first; the shader clock settles over ~20 launches")
-    ap.add_argument("--workload", type=int, default=3, help="1..5 (default 3)")
-    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "gemm"), default="fwd",
+    ap.add_argument("--workload", type=int, default=None,
+                    help="fwd/bwd 1..5, decode 1..3 (default 3); based 1..3 (default 2)")
+    ap.add_argument("--op", choices=("fwd", "bwd", "decode", "gemm", "based"), default="fwd",
                     help="the forward (default, the headline metric), the backward pass, or "
-                         "the decode-shaped split-KV forward, or the plain GEMM")
+                         "the decode-shaped split-KV forward, the plain GEMM, or Based linear "
+                         "attention")
     ap.add_argument("--gemm-shape", default="8192,8192,8192", help="M,N,K for --op gemm")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the oracle baseline sample")
@@ -349,6 +427,10 @@ def main() -> int:
 
     if args.op == "decode":
         return run_decode(args)
+    if args.workload is None:
+        args.workload = 2 if args.op == "based" else 3
+    if args.op == "based":
+        return run_based(args)
     if args.op == "gemm":
         return run_gemm(args)
 
