@@ -12,20 +12,22 @@
 // so that o_i = phi(q_i)^T S / phi(q_i)^T z with running sums S = sum phi(k_j) v_j^T
 // (273 x 64) and z = sum phi(k_j).
 //
-// gfx950 design: one workgroup of 4 waves per (batch, head) walks the sequence in chunks
-// of 64 tokens. The state S lives in MFMA accumulators (fp32) spread over the 4 waves:
-// wave w owns the 64 quadratic features with first index a in [4w, 4w + 4) for all 64
-// value columns, plus the linear and constant features for value columns [16w, 16w + 16).
-// For chunk c the waves split the 64 tokens (16 each) and compute
+// gfx950 design: one workgroup of 8 waves per (batch, head) walks the sequence in chunks
+// of 64 tokens, with two wave roles so that every SIMD overlaps one wave of each. The
+// state S lives in MFMA accumulators (fp32) of the 4 state waves: state wave u owns the 64
+// quadratic features with first index a in [4u, 4u + 4) for all 64 value columns, plus the
+// linear and constant features for value columns [16u, 16u + 16). For chunk c the 4
+// output waves split the 64 tokens (16 each) and compute
 //   * O_inter^T = S^T phi(Q_c)^T from a bf16 copy of S^T in LDS (written after chunk c-1),
 //   * O_intra^T = V_c^T W^T with W the causal Taylor weights inside the chunk,
 //   * the normaliser: t0 + q . ksum / 4 + q^T KK q / 32 in fp32, with KK = sum k k^T and
 //     ksum = sum k over earlier chunks (KK enters an MFMA as a bf16 hi + lo pair),
 //     plus the row sums of W,
-// then update their part of S with phi(K_c)^T V_c and publish the new bf16 S^T for the
-// next chunk. All products are v_mfma_f32_16x16x32_bf16. The quadratic features of K
+// while the state waves add phi(K_c)^T V_c to their part of S and publish the new bf16 S^T
+// for the next chunk. All products are v_mfma_f32_16x16x32_bf16. The quadratic features of K
 // are formed in registers: each lane holds k[token][b] for 8 tokens (transposing LDS
-// reads) and receives k[token][a] from lane a of its 16-lane row (DPP row broadcast).
+// reads) and multiplies by k[token][a] taken from lane a of its 16-lane row (a DPP row
+// broadcast folded into the multiply).
 // Chunk c+1's Q, K, V are copied global -> LDS (buffer_load ... lds) during chunk c;
 // rows past N read as zeros, so they add nothing to S, KK and ksum.
 #include <hip/hip_runtime.h>
@@ -44,7 +46,7 @@ using namespace attn_tile;
 constexpr int kD = 16;        // query/key features
 constexpr int kDv = 64;       // value features
 constexpr int kChunk = 64;    // tokens per chunk
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;  // 4 output waves + 4 state waves
 constexpr int kStRow = 296;   // bf16 per S^T row in LDS: 288 features + 8 (592-byte rows keep
                               // the 16-byte reads of 16 consecutive rows bank-conflict free)
 constexpr float kC2 = 0.17677669529663688f;  // 1 / (4 sqrt 2), the quadratic feature scale
@@ -74,9 +76,6 @@ struct BasedParams {
 // at j ^ swz_v(r). A transposing read covers, per 32 lanes, 8 consecutive rows and two
 // adjacent chunks; with this permutation those 8 rows land on 8 distinct bank ranges.
 __device__ inline int swz_v(int r) { return ((r >> 1) & 3) << 1; }
-
-__device__ inline float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ inline float bf_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
 
 __device__ inline bf16x8 pack8(const float (&x)[8]) {
   bf16x8 r;
@@ -113,61 +112,65 @@ __device__ inline bf16x4 tr4(const char* p) {
 
 // One wave's share of copying chunk `chunk` (rows past N read zeros: their offsets are
 // placed outside the buffer range on purpose). Copies 0-1: Q, 2-3: K (32 rows of 32 bytes
-// each), 4-11: V (8 rows of 128 bytes each, chunk-permuted); wave w issues 3w .. 3w + 2.
-__device__ inline void copy_chunk(const i32x4& qr, const i32x4& kr, const i32x4& vr, int chunk, int N,
-                                  uint32_t stage_lds, int w, int lane) {
-#pragma unroll
-  for (int u = 0; u < 3; ++u) {
-    const int i = 3 * w + u;
-    const int t0 = chunk * kChunk;
-    if (i < 4) {
-      const int row = 32 * (i & 1) + (lane >> 1);
-      const uint32_t voff = (t0 + row < N) ? (uint32_t)((t0 + row) * 32 + 16 * (lane & 1)) : 0x80000000u;
-      const uint32_t dst = stage_lds + (i < 2 ? 0 : kQBytes) + 1024 * (i & 1);
-      copy16_to_lds(i < 2 ? qr : kr, voff, 0, __builtin_amdgcn_readfirstlane(dst));
-    } else {
-      const int row = 8 * (i - 4) + (lane >> 3);
-      const int logical = (lane & 7) ^ swz_v(row);
-      const uint32_t voff = (t0 + row < N) ? (uint32_t)((t0 + row) * 128 + 16 * logical) : 0x80000000u;
-      const uint32_t dst = stage_lds + 2 * kQBytes + 1024 * (i - 4);
-      copy16_to_lds(vr, voff, 0, __builtin_amdgcn_readfirstlane(dst));
-    }
+// each), 4-11: V (8 rows of 128 bytes each, chunk-permuted). Output wave w issues copy w
+// (Q or K); state wave u issues copies 4 + 2u and 5 + 2u (V).
+__device__ inline void copy_one(const i32x4& qr, const i32x4& kr, const i32x4& vr, int i, int t0, int N,
+                                uint32_t stage_lds, int lane) {
+  if (i < 4) {
+    const int row = 32 * (i & 1) + (lane >> 1);
+    const uint32_t voff = (t0 + row < N) ? (uint32_t)((t0 + row) * 32 + 16 * (lane & 1)) : 0x80000000u;
+    const uint32_t dst = stage_lds + (i < 2 ? 0 : kQBytes) + 1024 * (i & 1);
+    copy16_to_lds(i < 2 ? qr : kr, voff, 0, __builtin_amdgcn_readfirstlane(dst));
+  } else {
+    const int row = 8 * (i - 4) + (lane >> 3);
+    const int logical = (lane & 7) ^ swz_v(row);
+    const uint32_t voff = (t0 + row < N) ? (uint32_t)((t0 + row) * 128 + 16 * logical) : 0x80000000u;
+    const uint32_t dst = stage_lds + 2 * kQBytes + 1024 * (i - 4);
+    copy16_to_lds(vr, voff, 0, __builtin_amdgcn_readfirstlane(dst));
   }
 }
 
-// The chunk loop of wave W (its features and tokens are compile-time).
+struct HeadRefs {
+  i32x4 qr, kr, vr;
+  __bf16* ob;
+  uint32_t smem_lds;
+};
+
+__device__ inline HeadRefs head_refs(const BasedParams& p, char* smem) {
+  const int N = p.N;
+  const size_t bh = blockIdx.x;
+  HeadRefs h;
+  h.qr = make_rsrc(p.q + bh * N * kD, (uint32_t)N * kD * 2);
+  h.kr = make_rsrc(p.k + bh * N * kD, (uint32_t)N * kD * 2);
+  h.vr = make_rsrc(p.v + bh * N * kDv, (uint32_t)N * kDv * 2);
+  h.ob = p.o + bh * N * kDv;
+  h.smem_lds = lds_address(smem);
+  return h;
+}
+
+// V^T fragment of the chunk in stage Vs for key step m and value columns 16 cb ..: tokens
+// 32 m + 4 g + j (j < 4) and 32 m + 16 + 4 g + j - 4, value column 16 cb + c.
+__device__ inline bf16x8 v_frag(const char* Vs, int m, int cb, int g, int c) {
+  const int r = 32 * m + 4 * g + (c >> 2);
+  const int chunk = (2 * cb + ((c & 3) >> 1)) ^ swz_v(r);
+  const char* a0 = Vs + r * 128 + 16 * chunk + 8 * (c & 1);
+  return __builtin_shufflevector(tr4(a0), tr4(a0 + 16 * 128), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Output wave W (0..3): the 16 query tokens 16W .. 16W + 15 of every chunk. Reads the bf16
+// S^T, KK and ksum published after the previous chunk; computes O_inter, O_intra, the
+// normaliser and stores o.
 template <int W>
-__device__ inline void based_wave(const BasedParams& p, char* smem, int lane) {
+__device__ inline void output_wave(const BasedParams& p, char* smem, int lane) {
   const int g = lane >> 4;  // 16-lane row
   const int c = lane & 15;  // lane within the row
   const int N = p.N;
-  const size_t bh = blockIdx.x;
-  const i32x4 qr = make_rsrc(p.q + bh * N * kD, (uint32_t)N * kD * 2);
-  const i32x4 kr = make_rsrc(p.k + bh * N * kD, (uint32_t)N * kD * 2);
-  const i32x4 vr = make_rsrc(p.v + bh * N * kDv, (uint32_t)N * kDv * 2);
-  __bf16* ob = p.o + bh * N * kDv;
-  const uint32_t smem_lds = lds_address(smem);
-
-  // S^T buffer 0, KK buffer 0 and ksum buffer 0 start at zero
-  for (int i = W * 64 + lane; i < kStBytes / 4; i += kWaves * 64) reinterpret_cast<uint32_t*>(smem + kOffSt)[i] = 0u;
-  for (int i = W * 64 + lane; i < kKKBytes / 4; i += kWaves * 64) reinterpret_cast<uint32_t*>(smem + kOffKK)[i] = 0u;
-  if (W == 0 && lane < kD) reinterpret_cast<float*>(smem + kOffKs)[lane] = 0.f;
-  copy_chunk(qr, kr, vr, 0, N, smem_lds, W, lane);
-
-  f32x4 sq[4][4];  // quadratic features (a = 4W + rb, b = 4g + i) x value columns 16cb + c
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) sq[rb][cb] = f32x4{};
-  f32x4 slin = {};   // linear features b = 4g + i (value / 2) x value columns 16W + c
-  f32x4 sconst = {}; // row 0: sum of v over value columns 16W + c; rows 1-15 stay zero
-  f32x4 kk = {};     // wave 0: KK[a = 4g + i][b = c]
-  float ksum_part = 0.f;  // wave 0: sum of k[token][c] over this lane's tokens
-
+  const HeadRefs hr = head_refs(p, smem);
+  copy_one(hr.qr, hr.kr, hr.vr, W, 0, N, hr.smem_lds, lane);
   wait_copies_and_barrier();
   for (int t = 0; t < p.n_chunks; ++t) {
     const int cur = t & 1;
-    if (t + 1 < p.n_chunks) copy_chunk(qr, kr, vr, t + 1, N, smem_lds + (cur ^ 1) * kStage, W, lane);
+    if (t + 1 < p.n_chunks) copy_one(hr.qr, hr.kr, hr.vr, W, (t + 1) * kChunk, N, hr.smem_lds + (cur ^ 1) * kStage, lane);
     const char* Qs = smem + cur * kStage;
     const char* Ks = Qs + kQBytes;
     const char* Vs = Ks + kQBytes;
@@ -218,19 +221,6 @@ __device__ inline void based_wave(const BasedParams& p, char* smem, int lane) {
       }
     }
 
-    // ---- V^T fragments of the chunk: tokens 32 m + 4 g + j (j < 4) and 32 m + 16 + 4 g + j - 4
-    bf16x8 vf[2][4];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int r = 32 * m + 4 * g + (c >> 2);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int chunk = (2 * cb + ((c & 3) >> 1)) ^ swz_v(r);
-        const char* a0 = Vs + r * 128 + 16 * chunk + 8 * (c & 1);
-        vf[m][cb] = __builtin_shufflevector(tr4(a0), tr4(a0 + 16 * 128), 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-    }
-
     // ---- intra-chunk: W^T for keys 16 kb + 4 g + i (kb <= W) against token tq
     float zpart = 0.f;
     float wv[4][4];
@@ -260,7 +250,8 @@ __device__ inline void based_wave(const BasedParams& p, char* smem, int lane) {
         bw[4 + i] = (__bf16)wv[2 * m + 1][i];
       }
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[m][cb], bw, o[cb], 0, 0, 0);
+      for (int cb = 0; cb < 4; ++cb)
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_frag(Vs, m, cb, g, c), bw, o[cb], 0, 0, 0);
     }
 
     // ---- normaliser: t0 + q . ksum / 4 + q^T KK q / 32 (earlier chunks) + row sum of W
@@ -290,42 +281,81 @@ __device__ inline void based_wave(const BasedParams& p, char* smem, int lane) {
         bf16x4 wo;
 #pragma unroll
         for (int i = 0; i < 4; ++i) wo[i] = (__bf16)(o[cb][i] * inv);
-        *reinterpret_cast<bf16x4*>(ob + (size_t)token * kDv + 16 * cb + 4 * g) = wo;
+        *reinterpret_cast<bf16x4*>(hr.ob + (size_t)token * kDv + 16 * cb + 4 * g) = wo;
       }
     }
+    wait_copies_and_barrier();
+  }
+}
 
-    // ---- state update with this chunk: S += phi(K)^T V, KK += K^T K, ksum += sum k
+// State wave U (0..3): owns the quadratic features with a in [4U, 4U + 4) for all value
+// columns and the linear and constant features of value columns 16U .. 16U + 15 (wave 0
+// also KK and ksum). Adds each chunk's contribution and publishes the bf16 S^T (and KK,
+// ksum) in the other buffer for the next chunk's output waves.
+template <int U>
+__device__ inline void state_wave(const BasedParams& p, char* smem, int lane) {
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const int N = p.N;
+  const HeadRefs hr = head_refs(p, smem);
+  copy_one(hr.qr, hr.kr, hr.vr, 4 + 2 * U, 0, N, hr.smem_lds, lane);
+  copy_one(hr.qr, hr.kr, hr.vr, 5 + 2 * U, 0, N, hr.smem_lds, lane);
+
+  f32x4 sq[4][4];  // quadratic features (a = 4U + rb, b = 4g + i) x value columns 16cb + c
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) sq[rb][cb] = f32x4{};
+  f32x4 slin = {};   // linear features b = 4g + i (value / 2) x value columns 16U + c
+  f32x4 sconst = {}; // row 0: sum of v over value columns 16U + c; rows 1-15 stay zero
+  f32x4 kk = {};     // wave 0: KK[a = 4g + i][b = c]
+  float ksum_part = 0.f;  // wave 0: sum of k[token][c] over this lane's tokens
+
+  wait_copies_and_barrier();
+  for (int t = 0; t < p.n_chunks; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < p.n_chunks) {
+      const uint32_t stage = hr.smem_lds + (cur ^ 1) * kStage;
+      copy_one(hr.qr, hr.kr, hr.vr, 4 + 2 * U, (t + 1) * kChunk, N, stage, lane);
+      copy_one(hr.qr, hr.kr, hr.vr, 5 + 2 * U, (t + 1) * kChunk, N, stage, lane);
+    }
+    const char* Ks = smem + cur * kStage + kQBytes;
+    const char* Vs = Ks + kQBytes;
+
+    // ---- S += phi(K)^T V, KK += K^T K, ksum += sum k
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const char* k0 = Ks + (32 * m + 4 * g + (c >> 2)) * 32 + 8 * (c & 3);
       const bf16x8 kc = __builtin_shufflevector(tr4(k0), tr4(k0 + 16 * 32), 0, 1, 2, 3, 4, 5, 6, 7);
-      float kf[8];
+      float kf[8], kfs[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) kf[j] = (float)kc[j];  // k[token_j][c]
-      const u32x4 kd = __builtin_bit_cast(u32x4, kc);
+      for (int j = 0; j < 8; ++j) {
+        kf[j] = (float)kc[j];  // k[token_j][c]
+        kfs[j] = kf[j] * kC2;
+      }
+      bf16x8 vfm[4];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) vfm[cb] = v_frag(Vs, m, cb, g, c);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         float f[8];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t ka = row_bcast_feature<W>(kd[d], rb);  // k[token][4W + rb]
-          f[2 * d] = bf_lo(ka) * (kf[2 * d] * kC2);
-          f[2 * d + 1] = bf_hi(ka) * (kf[2 * d + 1] * kC2);
-        }
+        for (int j = 0; j < 8; ++j)  // k[token_j][4U + rb] from lane 4U + rb of this row
+          f[j] = __uint_as_float(row_bcast_feature<U>(__float_as_uint(kf[j]), rb)) * kfs[j];
         const bf16x8 afeat = pack8(f);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
-          sq[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afeat, vf[m][cb], sq[rb][cb], 0, 0, 0);
+          sq[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afeat, vfm[cb], sq[rb][cb], 0, 0, 0);
       }
       float fl[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) fl[j] = 0.5f * kf[j];
-      slin = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(fl), vf[m][W], slin, 0, 0, 0);
+      slin = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(fl), vfm[U], slin, 0, 0, 0);
       bf16x8 ones;
 #pragma unroll
       for (int j = 0; j < 8; ++j) ones[j] = (__bf16)(c == 0 ? 1.f : 0.f);
-      sconst = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, vf[m][W], sconst, 0, 0, 0);
-      if (W == 0) {
+      sconst = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, vfm[U], sconst, 0, 0, 0);
+      if (U == 0) {
         kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, kc, kk, 0, 0, 0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) ksum_part += kf[j];
@@ -341,7 +371,7 @@ __device__ inline void based_wave(const BasedParams& p, char* smem, int lane) {
         bf16x4 x;
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = (__bf16)sq[rb][cb][i];
-        *reinterpret_cast<bf16x4*>(Stn + (16 * cb + c) * (kStRow * 2) + 2 * (16 * (4 * W + rb) + 4 * g)) = x;
+        *reinterpret_cast<bf16x4*>(Stn + (16 * cb + c) * (kStRow * 2) + 2 * (16 * (4 * U + rb) + 4 * g)) = x;
       }
     {
       bf16x4 xl, xc;
@@ -350,10 +380,10 @@ __device__ inline void based_wave(const BasedParams& p, char* smem, int lane) {
         xl[i] = (__bf16)slin[i];
         xc[i] = (__bf16)sconst[i];
       }
-      *reinterpret_cast<bf16x4*>(Stn + (16 * W + c) * (kStRow * 2) + 2 * (256 + 4 * g)) = xl;
-      *reinterpret_cast<bf16x4*>(Stn + (16 * W + c) * (kStRow * 2) + 2 * (272 + 4 * g)) = xc;
+      *reinterpret_cast<bf16x4*>(Stn + (16 * U + c) * (kStRow * 2) + 2 * (256 + 4 * g)) = xl;
+      *reinterpret_cast<bf16x4*>(Stn + (16 * U + c) * (kStRow * 2) + 2 * (272 + 4 * g)) = xc;
     }
-    if (W == 0) {
+    if (U == 0) {
       __bf16* KKn = reinterpret_cast<__bf16*>(smem + kOffKK + (cur ^ 1) * kKKBytes);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -368,14 +398,26 @@ __device__ inline void based_wave(const BasedParams& p, char* smem, int lane) {
   }
 }
 
-__global__ __launch_bounds__(256) void based_fwd_kernel(const BasedParams p) {
+// 8 waves: output waves 0-3 and state waves 4-7 (waves w and w + 4 share a SIMD, so every
+// SIMD runs one wave of each role). Both roles run n_chunks iterations with one barrier
+// each, after a common start: S^T buffer 0, KK buffer 0 and ksum buffer 0 are zeroed by all
+// waves before the first barrier.
+__global__ __launch_bounds__(512) void based_fwd_kernel(const BasedParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLds];
-  const int lane = threadIdx.x & 63;
-  switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-    case 0: based_wave<0>(p, smem, lane); break;
-    case 1: based_wave<1>(p, smem, lane); break;
-    case 2: based_wave<2>(p, smem, lane); break;
-    default: based_wave<3>(p, smem, lane); break;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  for (int i = tid; i < kStBytes / 4; i += 64 * kWaves) reinterpret_cast<uint32_t*>(smem + kOffSt)[i] = 0u;
+  for (int i = tid; i < kKKBytes / 4; i += 64 * kWaves) reinterpret_cast<uint32_t*>(smem + kOffKK)[i] = 0u;
+  if (tid < kD) reinterpret_cast<float*>(smem + kOffKs)[tid] = 0.f;
+  switch (__builtin_amdgcn_readfirstlane(tid >> 6)) {
+    case 0: output_wave<0>(p, smem, lane); break;
+    case 1: output_wave<1>(p, smem, lane); break;
+    case 2: output_wave<2>(p, smem, lane); break;
+    case 3: output_wave<3>(p, smem, lane); break;
+    case 4: state_wave<0>(p, smem, lane); break;
+    case 5: state_wave<1>(p, smem, lane); break;
+    case 6: state_wave<2>(p, smem, lane); break;
+    default: state_wave<3>(p, smem, lane); break;
   }
 }
 
