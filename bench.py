@@ -419,7 +419,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the attention forward runs on a single MI355X "
-              "and this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
+              "and the library has no multi-GPU path (use --gpus 1).", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
