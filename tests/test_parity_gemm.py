@@ -60,3 +60,23 @@ def test_gemm_writes_nothing_outside_c():
     assert (buf[:256] == 7.0).all() and (buf[256 + M * N:] == 7.0).all()
     ref = oracle.gemm_nt(a.double().cpu().numpy(), b.double().cpu().numpy())
     assert np.abs(c.double().cpu().numpy() - ref).max() <= 2.0 ** -8 * np.abs(ref).max() + 1e-3
+
+
+def test_gemm_bench_shape_sampled_rows():
+    """The launch the benchmark times (M = N = K = 8192): 16 rows of C (first, last, tile
+    edges and random ones) against the oracle, per element, and the whole C finite."""
+    M = N = K = 8192
+    a, b = rand((M, K), 8192), rand((N, K), 8193)
+    c = gemm_nt(a.cuda(), b.cuda())
+    torch.cuda.synchronize()
+    assert torch.isfinite(c.float()).all()
+    rng = np.random.default_rng(5)
+    rows = sorted({0, 1, 255, 256, 4095, 4096, 8191} | set(int(r) for r in rng.integers(0, M, 9)))
+    an, bn = a[rows].double().numpy(), b.double().numpy()
+    ref = oracle.gemm_nt(an, bn)
+    absprod = oracle.gemm_nt(np.abs(an), np.abs(bn))
+    bound = 2.0 ** -8 * np.abs(ref) + 2 * K * 2.0 ** -24 * absprod
+    got = c[rows].double().cpu().numpy()
+    err = np.abs(got - ref)
+    print(f"[parity-gemm] 8192^3 rows {rows}: max err/bound {float((err / bound).max()):.3f}", flush=True)
+    assert (err <= bound).all()
