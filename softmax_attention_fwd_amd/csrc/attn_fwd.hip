@@ -27,7 +27,9 @@
 //     global -> LDS by buffer_load ... lds into double-buffered rings; the K ring runs one
 //     tile ahead, so the score MFMAs of tile t+1 overlap the exponentials of tile t. The
 //     16-byte chunks of each tile row are permuted so that the K reads and the transposing
-//     V reads are free of LDS bank conflicts.
+//     V reads are free of LDS bank conflicts. In the ping-pong kernel one wave group issues
+//     all the copies, spaced out between its exponentials: issued in a burst, they queue
+//     at the compute unit's vector-memory path and stall every wave behind them.
 //   * the exp2 argument is fma(s, c, -m*c) with c = scale*log2(e) in fp32, on the fp32
 //     accumulator (the scale is never folded into bf16 Q). The running max only moves
 //     when a row's max grows by more than 2^8 (lazy rescaling), so O is rarely rescaled.
@@ -552,29 +554,36 @@ void attn_fwd_pp_kernel(const Params p) {
   const int ntiles = (wg_kv_end + kBc - 1) / kBc;
   const int T = !wave_active ? 0 : CAUSAL ? (min(N, q0 + kQW) + kBc - 1) / kBc : ntiles;
 
-  // K/V copies, shared by the 8 waves (the same layout and ragged-tile rule as
-  // attn_fwd_kernel)
+  // K/V copies (the layout and ragged-tile rule of attn_fwd_kernel). Only the four waves
+  // of group 1 copy, and in the steady state they spread their copies through their
+  // vector phase (see softmax): a copy instruction moves 1 KiB, and a burst of them from
+  // every wave at once queues at the compute unit's vector-memory path, stalling the
+  // issue of each wave behind it.
+  using LC = TileLayout<D, BC, kWavesPP / 2>;
+  const int cw = wave & 3;  // copy index of a group-1 wave
   const uint32_t head_bytes = (uint32_t)N * RB;
   const i32x4 krsrc = make_rsrc(p.k + head, head_bytes);
   const i32x4 vrsrc = make_rsrc(p.v + head, head_bytes);
-  uint32_t koff[L::kPeriodK], voff[L::kPeriodV];
+  uint32_t koff[LC::kPeriodK], voff[LC::kPeriodV];
 #pragma unroll
-  for (int i = 0; i < L::kPeriodK; ++i) {
-    const int row = (wave * L::kCopies + i) * L::kRowsPerCopy + lane / L::kChunks;
-    koff[i] = row * RB + (((lane % L::kChunks) ^ swz_k<D>(row)) << 4);
+  for (int i = 0; i < LC::kPeriodK; ++i) {
+    const int row = (cw * LC::kCopies + i) * LC::kRowsPerCopy + lane / LC::kChunks;
+    koff[i] = row * RB + (((lane % LC::kChunks) ^ swz_k<D>(row)) << 4);
   }
 #pragma unroll
-  for (int i = 0; i < L::kPeriodV; ++i) {
-    const int row = (wave * L::kCopies + i) * L::kRowsPerCopy + lane / L::kChunks;
-    voff[i] = row * RB + (((lane % L::kChunks) ^ swz_v<D>(row)) << 4);
+  for (int i = 0; i < LC::kPeriodV; ++i) {
+    const int row = (cw * LC::kCopies + i) * LC::kRowsPerCopy + lane / LC::kChunks;
+    voff[i] = row * RB + (((lane % LC::kChunks) ^ swz_v<D>(row)) << 4);
   }
   const uint32_t smem_lds = lds_address(smem);
-  auto copy_tile = [&](const i32x4& rsrc, const uint32_t* coff, int period, int t, uint32_t dst) {
+  // copies i0 .. i1-1 of this wave's share of tile t
+  auto copy_range = [&](const i32x4& rsrc, const uint32_t* coff, int period, int t, uint32_t dst,
+                        int i0, int i1) {
     const int key0 = t * kBc;
-    const uint32_t dst_w = dst + wave * L::kCopies * 1024;
+    const uint32_t dst_w = dst + cw * LC::kCopies * 1024;
     if (key0 + kBc <= N) {
 #pragma unroll
-      for (int i = 0; i < L::kCopies; ++i) {
+      for (int i = i0; i < i1; ++i) {
         const uint32_t soff = __builtin_amdgcn_readfirstlane(key0 * RB + (i / period) * period * 1024);
         copy16_to_lds(rsrc, coff[i % period], soff, dst_w + i * 1024);
       }
@@ -582,7 +591,7 @@ void attn_fwd_pp_kernel(const Params p) {
       const uint32_t last = (uint32_t)(N - key0 - 1);
       const uint32_t soff = __builtin_amdgcn_readfirstlane(key0 * RB);
 #pragma unroll
-      for (int i = 0; i < L::kCopies; ++i) {
+      for (int i = i0; i < i1; ++i) {
         const uint32_t o = coff[i % period] + (i / period) * period * 1024;
         copy16_to_lds(rsrc, (min(o / RB, last) * RB) | (o % RB), soff, dst_w + i * 1024);
       }
@@ -590,9 +599,9 @@ void attn_fwd_pp_kernel(const Params p) {
   };
   const uint32_t kbuf_lds[2] = {smem_lds, smem_lds + L::kTileBytes};
   const uint32_t vbuf_lds[2] = {smem_lds + 2 * L::kTileBytes, smem_lds + 3 * L::kTileBytes};
-  auto copy_k = [&](int t) { copy_tile(krsrc, koff, L::kPeriodK, t, kbuf_lds[t & 1]); };
-  auto copy_v = [&](int t) { copy_tile(vrsrc, voff, L::kPeriodV, t, vbuf_lds[t & 1]); };
-  copy_k(0);
+  auto copy_k = [&](int t, int i0, int i1) { copy_range(krsrc, koff, LC::kPeriodK, t, kbuf_lds[t & 1], i0, i1); };
+  auto copy_v = [&](int t, int i0, int i1) { copy_range(vrsrc, voff, LC::kPeriodV, t, vbuf_lds[t & 1], i0, i1); };
+  if (grp == 1) copy_k(0, 0, LC::kCopies);
 
   bf16x8 qf[D / 16];
   if (qrow < N) {
@@ -659,9 +668,26 @@ void attn_fwd_pp_kernel(const Params p) {
       }
     }
   };
+  // The copies of slot pair i (see below), one per part: this wave's share of K(i+1) in
+  // parts 0 .. kCopies-1, of V(i) in the rest. Only for pairs whose two tiles exist and
+  // are full, so that no branch separates the parts from the exponentials between them.
+  constexpr int kParts = 2 * LC::kCopies;
+  auto copy_part = [&](int i, int part) {
+    const bool isk = part < LC::kCopies;
+    const int t = isk ? i + 1 : i;
+    const i32x4& rsrc = isk ? krsrc : vrsrc;
+    const uint32_t dst = (isk ? kbuf_lds[t & 1] : vbuf_lds[t & 1]) + cw * LC::kCopies * 1024;
+    const int ci = isk ? part : part - LC::kCopies;
+    const int period = isk ? LC::kPeriodK : LC::kPeriodV;
+    const uint32_t off = isk ? koff[ci % LC::kPeriodK] : voff[ci % LC::kPeriodV];
+    const uint32_t soff = __builtin_amdgcn_readfirstlane(t * kBc * RB + (ci / period) * period * 1024);
+    copy16_to_lds(rsrc, off, soff, dst + ci * 1024);
+  };
   // vector phase of tile t: mask (a wave's last tile only), row max, lazy rescale,
-  // exponentials into pb and their sum into l
-  auto softmax = [&](int t, bool last) {
+  // exponentials into pb and their sum into l. With copy_pair >= 0 the copies of that
+  // slot pair go out one at a time, evenly spaced between the exponentials (the
+  // scheduling barriers keep them spread: 4 exponentials apart at D = 128).
+  auto softmax = [&](int t, bool last, int copy_pair) {
     if (last) {
       const int key0 = t * kBc;
       if ((key0 + kBc > N) || (CAUSAL && key0 + kBc - 1 > q0)) {
@@ -694,6 +720,12 @@ void attn_fwd_pp_kernel(const Params p) {
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        constexpr int kEvery = 16 * NB / kParts;
+        if (copy_pair >= 0 && (16 * j + r) % kEvery == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          copy_part(copy_pair, (16 * j + r) / kEvery);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][r], c, -mc));
         rs += e;
         pb[2 * j + (r >> 3)][r & 7] = (__bf16)e;
@@ -702,7 +734,8 @@ void attn_fwd_pp_kernel(const Params p) {
   };
 
   // Slot pairs i = 0 .. ntiles (two barriers each). The copies of K(i+1) and V(i) are
-  // issued at the start of pair i and waited for at its end; K(i+1) goes to the K slot
+  // issued by group 1 in the first slot of pair i (spread through its vector phase in the
+  // steady state) and waited for at the end of the pair; K(i+1) goes to the K slot
   // that held K(i-1), last read in pair i-1, and V(i) to the V slot that held V(i-2), last
   // read in pair i-1 too (two-slot rings). Group 0 runs, in pair i, the
   // matrix phase of step i (P V of tile i-1, scores of tile i) and then the vector phase of
@@ -710,8 +743,10 @@ void attn_fwd_pp_kernel(const Params p) {
   // Each group's sequence is straight-line code (first and last steps peeled), so the
   // accumulators keep their registers across the loop.
   auto copies = [&](int i) {
-    if (i + 1 < ntiles) copy_k(i + 1);
-    if (i < ntiles) copy_v(i);
+    if (grp == 1) {
+      if (i + 1 < ntiles) copy_k(i + 1, 0, LC::kCopies);
+      if (i < ntiles) copy_v(i, 0, LC::kCopies);
+    }
   };
   auto matrix = [&](int i) {  // P V of tile i-1 and scores of tile i, both present
     __builtin_amdgcn_s_setprio(2);
@@ -728,23 +763,23 @@ void attn_fwd_pp_kernel(const Params p) {
       qk(0);
       __syncthreads();
       if (T == 1) {
-        softmax(0, true);
+        softmax(0, true, -1);
       } else {
-        softmax(0, false);
+        softmax(0, false, -1);
       }
       wait_copies_and_barrier();
       for (i = 1; i + 1 < T; ++i) {
         copies(i);
         matrix(i);
         __syncthreads();
-        softmax(i, false);
+        softmax(i, false, -1);
         wait_copies_and_barrier();
       }
       if (i < T) {  // i == T - 1 >= 1
         copies(i);
         matrix(i);
         __syncthreads();
-        softmax(i, true);
+        softmax(i, true, -1);
         wait_copies_and_barrier();
         ++i;
       }
@@ -758,15 +793,24 @@ void attn_fwd_pp_kernel(const Params p) {
       __syncthreads();
       qk(0);
       wait_copies_and_barrier();
-      for (i = 1; i < T; ++i) {
+      // pairs whose copies are of full tiles (K(i+1) and V(i) end at or before N) spread
+      // them through the exponentials; the rest issue them at once
+      const int i_spread = min(T, min(ntiles, N / kBc) - 1);
+      for (i = 1; i < i_spread; ++i) {
+        softmax(i - 1, false, i);
+        __syncthreads();
+        matrix(i);
+        wait_copies_and_barrier();
+      }
+      for (; i < T; ++i) {
         copies(i);
-        softmax(i - 1, false);
+        softmax(i - 1, false, -1);
         __syncthreads();
         matrix(i);
         wait_copies_and_barrier();
       }
       copies(i);  // i == T
-      softmax(T - 1, true);
+      softmax(T - 1, true, -1);
       __syncthreads();
       pv(T - 1);
       wait_copies_and_barrier();
