@@ -47,10 +47,11 @@ struct GemmParams {
 // Rows at or past n_rows and columns at or past K are sent out of the buffer's range on
 // purpose and read zeros.
 __device__ inline void copy_slice(const i32x4& rsrc, int row0, int n_rows, int k0, int K,
-                                  uint32_t lds_tile, int wave, int lane) {
+                                  uint32_t lds_tile, int wave, int lane, int i0 = 0,
+                                  int i1 = kTileBytes / 1024 / kWaves) {
   constexpr int kChunks = kTk / 8;  // 8 chunks of 16 bytes per row
 #pragma unroll
-  for (int i = 0; i < kTileBytes / 1024 / kWaves; ++i) {
+  for (int i = i0; i < i1; ++i) {
     const int cidx = i * kWaves + wave;
     const int r = cidx * 8 + lane / kChunks;
     const int logical = (lane % kChunks) ^ swz<64>(r);
@@ -104,15 +105,25 @@ void gemm_nt_kernel(const GemmParams p) {
     for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x16{};
   const int rbase = row_read_base<64>(col, hi);
 
-  load(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  // The copies of the next slice go out a few at a time, one of A and one of B per 16-wide
+  // k step of the current slice, among its MFMAs. Issued all at once after the barrier (64
+  // KiB per compute unit), they queue at the vector-memory path and hold back the MFMAs
+  // behind them in every wave's instruction stream. The last slice is peeled so that the
+  // loop body has no branch around the copies.
+  constexpr int kPerStep = kTileBytes / 1024 / kWaves / (kTk / 16);
+  auto load_part = [&](int kt, int stage, int part) {
+    const uint32_t base = smem_lds + stage * kStageBytes;
+    copy_slice(arsrc, m0, p.M, kt * kTk, K, base, wave, lane, part * kPerStep, (part + 1) * kPerStep);
+    copy_slice(brsrc, n0, p.N, kt * kTk, K, base + kTileBytes, wave, lane, part * kPerStep, (part + 1) * kPerStep);
+  };
+  auto slice = [&](int kt, bool next) {
     const int stage = kt & 1;
     wait_copies_and_barrier();
-    if (kt + 1 < nk) load(kt + 1, stage ^ 1);
     const char* ta = smem + stage * kStageBytes + wm * kWaveM * kRowBytes;
     const char* tb = smem + stage * kStageBytes + kTileBytes + wn * kWaveN * kRowBytes;
 #pragma unroll
     for (int k16 = 0; k16 < kTk / 16; ++k16) {
+      if (next) load_part(kt + 1, stage ^ 1, k16);
       const int off = row_read_addr(rbase, k16);
       bf16x8 af[4], bf[2];
 #pragma unroll
@@ -126,7 +137,11 @@ void gemm_nt_kernel(const GemmParams p) {
         for (int mb = 0; mb < 4; ++mb)
           acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[nb], af[mb], acc[nb][mb], 0, 0, 0);
     }
-  }
+  };
+  load(0, 0);
+  int kt = 0;
+  for (; kt + 1 < nk; ++kt) slice(kt, true);
+  slice(kt, false);
 
   // register r of acc[nb][mb] holds C[m][n], m = m0 + 128wm + 32mb + col,
   // n = n0 + 64wn + 32nb + 8(r/4) + 4h + r%4: four consecutive n per (lane, r/4)
