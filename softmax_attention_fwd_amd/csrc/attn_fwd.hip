@@ -76,7 +76,6 @@ struct Params {
   int n_qtiles;  // ceil(N / kBr)
   int remap;     // 1: grid size is a multiple of 8, use the XCD-aware order
   float c;       // scale * log2(e)
-  int n_units;   // persistent kernel: B * H * n_qtiles work units
 };
 
 // Both halves of the wave receive max(x[lane], x[lane ^ 32]).
@@ -843,393 +842,6 @@ void attn_fwd_pp_kernel(const Params p) {
   }
 }
 
-// ---- persistent ping-pong kernel (D = 128, non-causal, N a multiple of 256). One
-// workgroup per compute unit walks its list of work units (b, h, 256-query tile) and runs
-// the slot pairs of all of them as one continuous stream of key tiles:
-//   * the K/V copies of a unit's first tiles go out during the previous unit's last pairs,
-//     exactly as if the two units' tiles were one sequence;
-//   * group 0 copies the next unit's Q tile global -> LDS (laid out like a K tile) during
-//     its vector phases two and three pairs before the unit ends, and each group reads it
-//     into its Q registers after the last score MFMA that needs the old Q;
-//   * each group stores its finished rows (O / l and lse) in the vector phase that opens
-//     the next unit, then restarts its softmax state.
-// Per unit this removes the workgroup launch, the round trips of the first Q and K/V
-// loads, and the half-empty first and last slots of the ping-pong pipeline. The phases,
-// their schedule and the per-row arithmetic are those of attn_fwd_pp_kernel, so the
-// results are bit-identical to the other kernels.
-template <int M>
-struct CopyMode {
-  static constexpr int value = M;  // 0: none, 1: K/V copies of the pair, 2: Q of the next unit
-};
-
-template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_pp_persistent_kernel(const Params p) {
-  static_assert(D == 128, "head dimension");
-  constexpr int W = kWavesPP;
-  constexpr int kBc = 64;
-  constexpr int NB = kBc / 32;
-  using L = TileLayout<D, kBc, W>;
-  using LC = TileLayout<D, kBc, W / 2>;  // copies are shared among four waves
-  constexpr int RB = L::kRowBytes;
-  constexpr int kQOff = L::kLdsBytes;        // LDS offset of the next unit's Q tile
-  constexpr int kParts = 2 * LC::kCopies;    // copies a wave spreads through one vector phase
-  static_assert(kBrPP * RB == 2 * kParts * (W / 2) * 1024, "Q tile = two vector phases of copies");
-  __shared__ __attribute__((aligned(1024))) char smem[L::kLdsBytes + kBrPP * RB];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;
-  const int cw = wave & 3;
-  const int col = lane & 31;
-  const int hi = lane >> 5;
-  const int N = p.N;
-  const float c = p.c;
-  const int T = N / kBc;  // key tiles per unit: a multiple of 4
-  const int G = gridDim.x;
-  const int R = (p.n_units - (int)blockIdx.x + G - 1) / G;  // units of this workgroup, >= 1
-  const uint32_t head_bytes = (uint32_t)N * RB;
-
-  // r-th unit of this workgroup -> head bh, query tile qt. Unit r is g' = r G + blockIdx;
-  // with G a multiple of 8, g' mod 8 is the XCD of the workgroup, and the remap gives each
-  // XCD a contiguous range of units (consecutive query tiles of the same heads).
-  auto unit = [&](int r, int& bh, int& qt) __attribute__((always_inline)) {
-    int g = r * G + (int)blockIdx.x;
-    if (p.remap) g = (g & 7) * (p.n_units >> 3) + (g >> 3);
-    bh = g / p.n_qtiles;
-    qt = g - bh * p.n_qtiles;
-  };
-  auto head_of = [&](int bh) __attribute__((always_inline)) { return (size_t)bh * (size_t)N * D; };
-
-  // copy lane offsets (the layout of attn_fwd_pp_kernel); the Q tile of the next unit is
-  // copied as four 64-row blocks laid out like K tiles, so it uses the K offsets
-  uint32_t koff[LC::kPeriodK], voff[LC::kPeriodV];
-#pragma unroll
-  for (int i = 0; i < LC::kPeriodK; ++i) {
-    const int row = (cw * LC::kCopies + i) * LC::kRowsPerCopy + lane / LC::kChunks;
-    koff[i] = row * RB + (((lane % LC::kChunks) ^ swz_k<D>(row)) << 4);
-  }
-#pragma unroll
-  for (int i = 0; i < LC::kPeriodV; ++i) {
-    const int row = (cw * LC::kCopies + i) * LC::kRowsPerCopy + lane / LC::kChunks;
-    voff[i] = row * RB + (((lane % LC::kChunks) ^ swz_v<D>(row)) << 4);
-  }
-  const uint32_t smem_lds = lds_address(smem);
-  // LDS addresses of the ring slots (K slot t & 1, V slot t & 1)
-  auto kslot = [&](int t) __attribute__((always_inline)) { return smem_lds + (uint32_t)((t & 1) * L::kTileBytes); };
-  auto vslot = [&](int t) __attribute__((always_inline)) { return smem_lds + (uint32_t)((2 + (t & 1)) * L::kTileBytes); };
-  // copy i of this wave's share of a tile: K (isk) or V, source rsrc at scalar offset soff
-  // (the scalar operands are uniform; readfirstlane states it for the compiler, which
-  // cannot always prove it through the copy-source variables below)
-  auto copy_one = [&](bool isk, const i32x4& rsrc, uint32_t soff, uint32_t dst, int i) __attribute__((always_inline)) {
-    const int period = isk ? LC::kPeriodK : LC::kPeriodV;
-    const uint32_t off = isk ? koff[i % LC::kPeriodK] : voff[i % LC::kPeriodV];
-    const uint32_t s = __builtin_amdgcn_readfirstlane(soff + (i / period) * period * 1024);
-    i32x4 rs;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) rs[e] = __builtin_amdgcn_readfirstlane(rsrc[e]);
-    copy16_to_lds(rs, off, s, __builtin_amdgcn_readfirstlane(dst + cw * LC::kCopies * 1024 + i * 1024));
-  };
-  auto copy_tile = [&](bool isk, const i32x4& rsrc, int t, uint32_t dst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LC::kCopies; ++i) copy_one(isk, rsrc, (uint32_t)(t * kBc * RB), dst, i);
-  };
-
-  // the sources of the copies spread through a vector phase (set before each call)
-  i32x4 cp_krsrc, cp_vrsrc, cp_qrsrc;
-  uint32_t cp_ksoff = 0, cp_vsoff = 0, cp_kdst = 0, cp_vdst = 0, cp_qsoff = 0;
-  int cp_qpart0 = 0;
-  auto copy_kv_part = [&](int part) __attribute__((always_inline)) {
-    if (part < LC::kCopies) copy_one(true, cp_krsrc, cp_ksoff, cp_kdst, part);
-    else copy_one(false, cp_vrsrc, cp_vsoff, cp_vdst, part - LC::kCopies);
-  };
-  // part j of the next unit's Q tile: 64-row block j / kCopies, copy j % kCopies of it
-  auto copy_q_part = [&](int j) __attribute__((always_inline)) {
-    const int b = j / LC::kCopies, i = j % LC::kCopies;
-    copy_one(true, cp_qrsrc, cp_qsoff + (uint32_t)(b * kBc * RB), smem_lds + kQOff + b * L::kTileBytes, i);
-  };
-
-  // ---- the first unit: its K tile 0 (group 1) and Q rows (from global memory)
-  int bh0, qt0;
-  unit(0, bh0, qt0);
-  if (grp == 1) copy_tile(true, make_rsrc(p.k + head_of(bh0), head_bytes), 0, kslot(0));
-  bf16x8 qf[D / 16];
-  {
-    const int qrow = qt0 * kBrPP + wave * kQW + col;
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(p.q + head_of(bh0) + (size_t)qrow * D) + hi;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = src[2 * s];
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-
-  int k_addr[D / 16];
-#pragma unroll
-  for (int st = 0; st < D / 16; ++st) k_addr[st] = col * RB + 16 * ((2 * st + hi) ^ swz_k<D>(col));
-  const int jj = lane & 15;
-  const int gq = lane >> 4;
-  int v_addr[D / 32];
-#pragma unroll
-  for (int d = 0; d < D / 32; ++d) {
-    const int row = 4 * hi + (jj >> 2);
-    const int chunk = 4 * d + 2 * (gq & 1) + ((jj >> 1) & 1);
-    v_addr[d] = row * RB + 16 * (chunk ^ swz_v<D>(row)) + 8 * (jj & 1);
-  }
-
-  float m = -INFINITY;
-  float l = 0.f;
-  f32x16 o[D / 32];
-#pragma unroll
-  for (int d = 0; d < D / 32; ++d) o[d] = f32x16{};
-  f32x16 s[NB];
-  bf16x8 pb[2 * NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) s[j] = f32x16{};
-#pragma unroll
-  for (int j = 0; j < 2 * NB; ++j) pb[j] = bf16x8{};
-
-  auto qk = [&](int t) __attribute__((always_inline)) {  // scores of tile t (K slot t & 1)
-    const int kb = (t & 1) * L::kTileBytes;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) s[j] = f32x16{};
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const char* a = smem + kb + k_addr[st] + 32 * j * RB;
-        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a), qf[st],
-                                                       s[j], 0, 0, 0);
-      }
-    }
-  };
-  auto pv = [&](int t) __attribute__((always_inline)) {  // O^T += V^T P^T of tile t (V slot t & 1; t = -1 is slot 1)
-    const int vb = 2 * L::kTileBytes + (t & 1) * L::kTileBytes;
-#pragma unroll
-    for (int st = 0; st < kBc / 16; ++st) {
-#pragma unroll
-      for (int d = 0; d < D / 32; ++d) {
-        const char* a0 = smem + vb + v_addr[d] + 16 * st * RB;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a0);
-        const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
-        const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[d], 0, 0, 0);
-      }
-    }
-  };
-  auto matrix = [&](int t) __attribute__((always_inline)) {  // P V of the tile before t, then the scores of tile t
-    __builtin_amdgcn_s_setprio(2);
-    pv(t - 1);
-    qk(t);
-    matrix_phase_schedule<D, kBc>();
-    __builtin_amdgcn_s_setprio(0);
-  };
-  auto last_pv = [&](int t) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_setprio(2);
-    pv(t);
-    __builtin_amdgcn_s_setprio(0);
-  };
-  // vector phase: row max, lazy rescale, exponentials into pb and their sum into l; the
-  // copies of the mode go out one at a time, evenly spaced between the exponentials
-  auto softmax = [&](auto mode) __attribute__((always_inline)) {
-    constexpr int kMode = decltype(mode)::value;
-    float mx = m;
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
-    mx = max_across_halves(mx);
-    if (__builtin_amdgcn_ballot_w64((mx - m) * c > kRescaleLog2)) {
-      const float alpha = __builtin_amdgcn_exp2f((m - mx) * c);
-      m = mx;
-      l *= alpha;
-#pragma unroll
-      for (int d = 0; d < D / 32; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-    }
-    const float mc = m * c;
-    float rs = 0.f;
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        constexpr int kEvery = 16 * NB / kParts;
-        if constexpr (kMode != 0) {
-          if ((16 * j + r) % kEvery == 0) {
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (kMode == 1) copy_kv_part((16 * j + r) / kEvery);
-            else copy_q_part(cp_qpart0 + (16 * j + r) / kEvery);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][r], c, -mc));
-        rs += e;
-        pb[2 * j + (r >> 3)][r & 7] = (__bf16)e;
-      }
-    l += rs;
-  };
-  auto load_q_lds = [&]() __attribute__((always_inline)) {  // this wave's 32 rows of the next unit's Q tile
-    // The empty asm makes the base opaque here, so the compiler cannot hoist the eight
-    // address sums out of the loops and keep them in registers for the whole kernel.
-    int base = kQOff + wave * kQW * RB;
-    asm volatile("" : "+s"(base));
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-      qf[st] = *reinterpret_cast<const bf16x8*>(smem + base + k_addr[st]);
-  };
-  // O / l in bf16 (round to nearest even) and lse of unit r, then a fresh softmax state
-  auto store_and_reset = [&](int r) __attribute__((always_inline)) {
-    int bh, qt;
-    unit(r, bh, qt);
-    const int qrow = qt * kBrPP + wave * kQW + col;
-    const float lt = sum_across_halves(l);
-    const float inv = 1.f / lt;
-    __bf16* orow = p.o + head_of(bh) + (size_t)qrow * D;
-#pragma unroll
-    for (int d = 0; d < D / 32; ++d)
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        bf16x4 w;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = (__bf16)(o[d][4 * j4 + i] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * j4 + 4 * hi) = w;
-      }
-    if (hi == 0) p.lse[(size_t)bh * N + qrow] = (m * c + __builtin_log2f(lt)) * kLn2;
-    m = -INFINITY;
-    l = 0.f;
-#pragma unroll
-    for (int d = 0; d < D / 32; ++d) o[d] = f32x16{};
-  };
-
-  // Slot pairs run over the concatenated tiles of the units (T per unit): in pair (r, t)
-  // group 0 runs the matrix phase of tile t (P V of the tile before it, which at t = 0 is
-  // the previous unit's last) and then the vector phase of tile t; group 1 runs the
-  // vector phase of the tile before t and then the matrix phase of tile t, and copies K of
-  // the tile after t (the next unit's tile 0 at t = T - 1) and V of tile t. Ring slots
-  // follow the tile parity (T is even). Each group executes two barriers per pair.
-  wait_copies_and_barrier();
-  if (grp == 0) {
-    qk(0);
-    __syncthreads();
-    softmax(CopyMode<0>{});
-    __syncthreads();
-    for (int r = 0; r < R; ++r) {
-      const bool more = r + 1 < R;
-      if (more) {
-        int bhn, qtn;
-        unit(r + 1, bhn, qtn);
-        cp_qrsrc = make_rsrc(p.q + head_of(bhn), head_bytes);
-        cp_qsoff = (uint32_t)(qtn * kBrPP * RB);
-      }
-      int t = 1;
-      for (; t < T - 3; ++t) {
-        matrix(t);
-        __syncthreads();
-        softmax(CopyMode<0>{});
-        __syncthreads();
-      }
-      for (; t < T - 1; ++t) {  // t = T-3, T-2: the next unit's Q tile, half per pair
-        matrix(t);
-        __syncthreads();
-        if (more) {
-          cp_qpart0 = (t == T - 3) ? 0 : kParts;
-          softmax(CopyMode<2>{});
-          wait_copies_and_barrier();
-        } else {
-          softmax(CopyMode<0>{});
-          __syncthreads();
-        }
-      }
-      matrix(T - 1);
-      __syncthreads();
-      softmax(CopyMode<0>{});
-      if (more) load_q_lds();
-      __syncthreads();
-      if (more) {  // pair (r + 1, 0)
-        matrix(0);
-        __syncthreads();
-        store_and_reset(r);
-        softmax(CopyMode<0>{});
-        __syncthreads();
-      } else {  // the final pair
-        last_pv(T - 1);
-        __syncthreads();
-        store_and_reset(r);
-        __syncthreads();
-      }
-    }
-  } else {
-    {  // pair (0, 0): K(0, 1) and V(0, 0) at once
-      const size_t h0 = head_of(bh0);
-      copy_tile(true, make_rsrc(p.k + h0, head_bytes), 1, kslot(1));
-      copy_tile(false, make_rsrc(p.v + h0, head_bytes), 0, vslot(0));
-    }
-    __syncthreads();
-    qk(0);
-    wait_copies_and_barrier();
-    for (int r = 0; r < R; ++r) {
-      const bool more = r + 1 < R;
-      int bh, qt, bhn = 0, qtn = 0;
-      unit(r, bh, qt);
-      if (more) unit(r + 1, bhn, qtn);
-      const i32x4 krsrc = make_rsrc(p.k + head_of(bh), head_bytes);
-      const i32x4 vrsrc = make_rsrc(p.v + head_of(bh), head_bytes);
-      const i32x4 knrsrc = make_rsrc(p.k + head_of(bhn), head_bytes);
-      // pairs (r, 1 .. T-2): K(r, t + 1) and V(r, t), spread through the exponentials
-      auto kv_pair = [&](int t) __attribute__((always_inline)) {
-        cp_krsrc = krsrc;
-        cp_ksoff = (uint32_t)((t + 1) * kBc * RB);
-        cp_kdst = kslot((t + 1) & 1);
-        cp_vrsrc = vrsrc;
-        cp_vsoff = (uint32_t)(t * kBc * RB);
-        cp_vdst = vslot(t & 1);
-        softmax(CopyMode<1>{});
-        __syncthreads();
-        matrix(t);
-        wait_copies_and_barrier();
-      };
-      if (r > 0) store_and_reset(r - 1);
-      kv_pair(1);
-      for (int t = 2; t < T - 1; ++t) kv_pair(t);
-      // pair (r, T - 1): K(r + 1, 0), if there is a next unit, and V(r, T - 1)
-      if (more) {
-        cp_krsrc = knrsrc;
-        cp_ksoff = 0;
-        cp_kdst = kslot(0);
-        cp_vrsrc = vrsrc;
-        cp_vsoff = (uint32_t)((T - 1) * kBc * RB);
-        cp_vdst = vslot(1);
-        softmax(CopyMode<1>{});
-      } else {
-        copy_tile(false, vrsrc, T - 1, vslot(1));
-        softmax(CopyMode<0>{});
-      }
-      __syncthreads();
-      matrix(T - 1);
-      wait_copies_and_barrier();
-      if (more) {  // pair (r + 1, 0): K(r + 1, 1) and V(r + 1, 0)
-        cp_krsrc = knrsrc;
-        cp_ksoff = (uint32_t)(kBc * RB);
-        cp_kdst = kslot(1);
-        cp_vrsrc = make_rsrc(p.v + head_of(bhn), head_bytes);
-        cp_vsoff = 0;
-        cp_vdst = vslot(0);
-        softmax(CopyMode<1>{});
-        load_q_lds();
-        __syncthreads();
-        matrix(0);
-        wait_copies_and_barrier();
-      } else {  // the final pair
-        softmax(CopyMode<0>{});
-        __syncthreads();
-        last_pv(T - 1);
-        __syncthreads();
-      }
-    }
-    store_and_reset(R - 1);
-  }
-}
-
 template <int D, int BC, int W>
 void launch(int causal, dim3 grid, hipStream_t s, const Params& p) {
   const dim3 block(64 * W);
@@ -1237,25 +849,19 @@ void launch(int causal, dim3 grid, hipStream_t s, const Params& p) {
   else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, W, false>), grid, block, 0, s, p);
 }
 
-// Kernel choice. D = 128 runs a ping-pong kernel: the persistent one when it applies
-// (non-causal, N a multiple of 256: every unit then has the same number of full key
-// tiles), else the one-unit-per-workgroup one. D = 64 runs the four-wave kernel: its
+// Kernel choice. D = 128 runs the ping-pong kernel; D = 64 runs the four-wave kernel: its
 // vector work per key tile is that of D = 128 while its matrix work halves, so the two
 // phases of a ping-pong pair would not balance (measured slower). Two environment
 // variables, read at every call so that tests can exercise each path in one process,
-// override the choice for testing and tuning: ATTN_FWD_KERNEL=persistent|pingpong|fourwave
-// (persistent falls back to pingpong where it does not apply), and ATTN_FWD_BC=32|64 for
-// the key tile of the four-wave kernel.
-enum class Kernel { kPersistent, kPingPong, kFourWave };
+// override the choice for testing and tuning: ATTN_FWD_KERNEL=pingpong|fourwave, and
+// ATTN_FWD_BC=32|64 for the key tile of the four-wave kernel.
+enum class Kernel { kPingPong, kFourWave };
 
-Kernel choose_kernel(int D, int N, int causal) {
-  const bool persistent_ok = D == 128 && !causal && N % kBrPP == 0;
+Kernel choose_kernel(int D) {
   const char* e = getenv("ATTN_FWD_KERNEL");
-  if (e && strcmp(e, "persistent") == 0) return persistent_ok ? Kernel::kPersistent : Kernel::kPingPong;
   if (e && strcmp(e, "pingpong") == 0) return Kernel::kPingPong;
   if (e && strcmp(e, "fourwave") == 0) return Kernel::kFourWave;
-  if (D == 64) return Kernel::kFourWave;
-  return persistent_ok ? Kernel::kPersistent : Kernel::kPingPong;
+  return D == 128 ? Kernel::kPingPong : Kernel::kFourWave;
 }
 
 int key_tile() {
@@ -1302,25 +908,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.n_qtiles = (int)n_qtiles;
   p.remap = (grid % 8 == 0) ? 1 : 0;
   p.c = scale * kLog2e;
-  p.n_units = 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const Kernel kernel = choose_kernel(D, N, causal);
-  if (kernel == Kernel::kPersistent) {
-    // one workgroup per compute unit of the current device (one fits per CU: 512
-    // threads, 128 KiB of LDS), each walking units g' = blockIdx + r * grid
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-      return ATTN_FWD_ELAUNCH;
-    const int64_t n_qtiles_pp = N / kBrPP;
-    const int64_t units = (int64_t)B * H * n_qtiles_pp;
-    const int64_t grid_ps = units < cus ? units : cus;
-    p.n_qtiles = (int)n_qtiles_pp;
-    p.n_units = (int)units;
-    p.remap = (units % 8 == 0 && grid_ps % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((attn_fwd_pp_persistent_kernel<128>), dim3((unsigned)grid_ps), dim3(64 * kWavesPP), 0, s, p);
-  } else if (kernel == Kernel::kPingPong) {
+  if (choose_kernel(D) == Kernel::kPingPong) {
     const int64_t n_qtiles_pp = ((int64_t)N + kBrPP - 1) / kBrPP;
     const int64_t grid_pp = (int64_t)B * H * n_qtiles_pp;
     p.n_qtiles = (int)n_qtiles_pp;
