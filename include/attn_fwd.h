@@ -54,14 +54,17 @@ extern "C" {
  *
  * Ownership: the caller owns every buffer. The library allocates no device memory, keeps
  * no state between calls, and may be called concurrently from several host threads on
- * different streams. Each call reads two testing and tuning variables from the
- * environment: ATTN_FWD_KERNEL=pingpong|fourwave overrides the kernel chosen by head
- * dimension (ping-pong for D = 128, four-wave for D = 64; both give identical results),
- * and ATTN_FWD_BC=32 selects 32-key tiles in the four-wave kernel (default 64).
+ * different streams. The kernel is chosen by shape: ping-pong for D = 128; for D = 64,
+ * ping-pong when causal == 0 and B * H * ceil(N / 256) is at least the compute-unit count
+ * of the current device (which the call queries), else four-wave. Both give identical
+ * results. Each call reads two testing and tuning variables from the environment:
+ * ATTN_FWD_KERNEL=pingpong|fourwave overrides that choice, and ATTN_FWD_BC=32 selects
+ * 32-key tiles in the four-wave kernel (default 64).
  *
  * Behaviour: arguments are validated on the host before any HIP call; an invalid call
  * returns a negative code and enqueues nothing. A valid call enqueues one kernel and
- * returns without synchronising; errors raised later by the device are reported by the
+ * returns without synchronising (ATTN_FWD_ELAUNCH also covers a failed query of the
+ * compute-unit count); errors raised later by the device are reported by the
  * HIP runtime on the stream, not by this function. Nothing is printed.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

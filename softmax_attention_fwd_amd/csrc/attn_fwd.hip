@@ -11,11 +11,11 @@
 //
 // gfx950 design (not the H100 one):
 //   * each wave owns 32 query rows. Two kernels share the per-row arithmetic below and give
-//     identical results: at D = 128 the ping-pong kernel (8 waves, 256 queries per
-//     workgroup, one workgroup per compute unit, two wave groups alternating matrix and
-//     vector phases on every SIMD); at D = 64 the four-wave kernel (128 queries per
-//     workgroup, two workgroups per compute unit, each wave interleaving its own MFMAs and
-//     exponentials).
+//     identical results: the ping-pong kernel (8 waves, 256 queries per workgroup, one
+//     workgroup per compute unit, two wave groups alternating matrix and vector phases on
+//     every SIMD), used at D = 128 and for non-causal D = 64 on grids that fill the device;
+//     and the four-wave kernel (128 queries per workgroup, two workgroups per compute
+//     unit, each wave interleaving its own MFMAs and exponentials), used otherwise.
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: lane l
 //     then holds 16 keys of query (l % 32) per 32-key block, so the row max and row sum
 //     are in-lane reductions plus one v_permlane32_swap between the two lane halves.
@@ -849,19 +849,24 @@ void launch(int causal, dim3 grid, hipStream_t s, const Params& p) {
   else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, W, false>), grid, block, 0, s, p);
 }
 
-// Kernel choice. D = 128 runs the ping-pong kernel; D = 64 runs the four-wave kernel: its
-// vector work per key tile is that of D = 128 while its matrix work halves, so the two
-// phases of a ping-pong pair would not balance (measured slower). Two environment
-// variables, read at every call so that tests can exercise each path in one process,
-// override the choice for testing and tuning: ATTN_FWD_KERNEL=pingpong|fourwave, and
-// ATTN_FWD_BC=32|64 for the key tile of the four-wave kernel.
+// Kernel choice. D = 128 runs the ping-pong kernel. D = 64 runs the ping-pong kernel when
+// the mask is off and its grid (one workgroup of 256 queries per compute unit) fills the
+// device, else the four-wave kernel. At D = 64 a vector phase costs as much as at D = 128
+// while a matrix phase halves; measured on MI355X (interleaved, 200 launches each), the
+// ping-pong kernel is still 3-7% faster non-causal (B16 H16 N1024 to B1 H32 N4096), but
+// 10% slower causal, where the waves of a workgroup stop at different diagonal tiles, and
+// slower on grids that leave compute units idle (B1 H4 N8192: 570 vs 630 TFLOP/s). Two
+// environment variables, read at every call so that tests can exercise each path in one
+// process, override the choice for testing and tuning: ATTN_FWD_KERNEL=pingpong|fourwave,
+// and ATTN_FWD_BC=32|64 for the key tile of the four-wave kernel.
 enum class Kernel { kPingPong, kFourWave };
 
-Kernel choose_kernel(int D) {
+Kernel choose_kernel(int D, int64_t pp_grid, int causal, int cus) {
   const char* e = getenv("ATTN_FWD_KERNEL");
   if (e && strcmp(e, "pingpong") == 0) return Kernel::kPingPong;
   if (e && strcmp(e, "fourwave") == 0) return Kernel::kFourWave;
-  return D == 128 ? Kernel::kPingPong : Kernel::kFourWave;
+  if (D == 128) return Kernel::kPingPong;
+  return (!causal && pp_grid >= cus) ? Kernel::kPingPong : Kernel::kFourWave;
 }
 
 int key_tile() {
@@ -910,9 +915,16 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   p.c = scale * kLog2e;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (choose_kernel(D) == Kernel::kPingPong) {
-    const int64_t n_qtiles_pp = ((int64_t)N + kBrPP - 1) / kBrPP;
-    const int64_t grid_pp = (int64_t)B * H * n_qtiles_pp;
+  const int64_t n_qtiles_pp = ((int64_t)N + kBrPP - 1) / kBrPP;
+  const int64_t grid_pp = (int64_t)B * H * n_qtiles_pp;
+  int cus = 0;
+  if (D == 64 && !causal) {  // the compute units of the current device decide the D = 64 kernel
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return ATTN_FWD_ELAUNCH;
+  }
+  if (choose_kernel(D, grid_pp, causal, cus) == Kernel::kPingPong) {
     p.n_qtiles = (int)n_qtiles_pp;
     p.remap = (grid_pp % 8 == 0) ? 1 : 0;
     const dim3 gpp((unsigned)grid_pp), bpp(64 * kWavesPP);

@@ -90,8 +90,9 @@ def test_small_shapes_full_oracle(B, H, N, D, causal, sigma):
     check(o, lse, o_ref, lse_ref, f"B{B} H{H} N{N} D{D} causal={causal} sigma={sigma}")
 
 
-# Both forward kernels (ping-pong, the D = 128 default, and four-wave, the D = 64 default)
-# are selectable per call through ATTN_FWD_KERNEL. They perform the same per-row arithmetic
+# Both forward kernels (ping-pong, the D = 128 default and the non-causal D = 64 default on
+# grids that fill the device, and four-wave, the other D = 64 default) are selectable per
+# call through ATTN_FWD_KERNEL. They perform the same per-row arithmetic
 # in the same order, so their outputs must agree bit for bit; each is also held to the
 # oracle on the non-default head dimension. The shapes include grids of more workgroups
 # than the GPU holds at once.
