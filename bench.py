@@ -49,7 +49,7 @@ KERNEL_SOURCE = os.path.join(ROOT, "softmax_attention_fwd_amd", "csrc", "attn_fw
 # reports null.
 MEASURED_TRAFFIC = {
     "w3_b16h16n4096d128": {
-        "source_sha256": "0f69fd5f85fffb1e386a9ba2c4d0b786308e2890dd08fe77aa61d42ab2fe28d8",
+        "source_sha256": "32f0b38a7626e2aabf59c38e0dc4f03c7dd26120a4920c01bf13aa03a9a56cc7",
         "fetch_kib": 393391.89 * 2.0,
         "write_kib": 266240.0 * 1.0,
     },
