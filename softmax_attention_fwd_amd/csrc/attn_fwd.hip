@@ -485,8 +485,8 @@ void attn_fwd_kernel(const Params p) {
   }
 }
 
-// ---- ping-pong kernel (the D = 128 path): one workgroup of 8 waves (two per SIMD, one
-// workgroup per compute unit) covers 256 queries. The waves form two groups (waves 0-3 and
+// ---- ping-pong kernel (D = 128, and non-causal D = 64 on grids that fill the device): one
+// workgroup of 8 waves (two per SIMD, one workgroup per compute unit) covers 256 queries. The waves form two groups (waves 0-3 and
 // 4-7; waves w and w + 4 share a SIMD) that run the same sequence of phases offset by one:
 // a matrix phase (P V of tile j - 1, then the scores of tile j: MFMAs and the LDS reads
 // feeding them) and a vector phase (mask, row max, lazy rescale and exponentials of tile
@@ -531,7 +531,12 @@ void attn_fwd_pp_kernel(const Params p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;
+  // Waves w and w + 4 share a SIMD, and waves 0-3 are dispatched first: on every SIMD they
+  // are the older wave. The younger wave's matrix phase beside the older wave's dense
+  // exponentials ran about 20% longer than the reverse pairing (instrumented, 1632 vs 1340
+  // cycles), so the older waves form group 1 (vector phase first, with the copies) and the
+  // younger ones group 0; both matrix phases then take about 1330 cycles.
+  const int grp = (wave >> 2) ^ 1;
   const int col = lane & 31;
   const int hi = lane >> 5;
 
