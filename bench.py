@@ -49,7 +49,7 @@ KERNEL_SOURCE = os.path.join(ROOT, "softmax_attention_fwd_amd", "csrc", "attn_fw
 # reports null.
 MEASURED_TRAFFIC = {
     "w3_b16h16n4096d128": {
-        "source_sha256": "f27ae95633eae39d8420fc9cfddc592feb3321de548eb804104c9cf7655d7943",
+        "source_sha256": "92622d3c60e217c7ccfaf74b86b883caac2d051487d501e345044447cf083003",
         "fetch_kib": 393392.04 * 2.0,
         "write_kib": 266242.59 * 1.0,
     },

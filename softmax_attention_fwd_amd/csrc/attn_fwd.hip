@@ -486,8 +486,9 @@ void attn_fwd_kernel(const Params p) {
 }
 
 // ---- ping-pong kernel (D = 128, and non-causal D = 64 on grids that fill the device): one
-// workgroup of 8 waves (two per SIMD, one workgroup per compute unit) covers 256 queries. The waves form two groups (waves 0-3 and
-// 4-7; waves w and w + 4 share a SIMD) that run the same sequence of phases offset by one:
+// workgroup of 8 waves (two per SIMD, one workgroup per compute unit) covers 256 queries.
+// The waves form two groups (waves 0-3 are group 1, waves 4-7 group 0; waves w and w + 4
+// share a SIMD) that run the same sequence of phases offset by one:
 // a matrix phase (P V of tile j - 1, then the scores of tile j: MFMAs and the LDS reads
 // feeding them) and a vector phase (mask, row max, lazy rescale and exponentials of tile
 // j). A workgroup barrier ends every phase, so on every SIMD one wave's MFMAs run while
