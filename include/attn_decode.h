@@ -37,7 +37,12 @@ extern "C" {
                                          workspace not 256-byte aligned                      */
 #define ATTN_DECODE_ELAUNCH      -4   /* hipGetLastError() was set after the launches (also
                                          reports, and clears, an earlier pending error)      */
-#define ATTN_DECODE_EWORKSPACE   -5   /* workspace_bytes < attn_decode_workspace_bytes(...)   */
+#define ATTN_DECODE_EWORKSPACE   -5   /* workspace_bytes < attn_decode_workspace_bytes(...);
+                                         attn_decode_noalloc: that size exceeds
+                                         ATTN_DECODE_NOALLOC_MAX_WORKSPACE                 */
+
+/* Size of the fixed device scratch of attn_decode_noalloc: 33 MiB. */
+#define ATTN_DECODE_NOALLOC_MAX_WORKSPACE ((size_t)33 << 20)
 
 /*
  * attn_decode_workspace_bytes - device workspace attn_decode needs: the partial outputs
@@ -65,6 +70,32 @@ size_t attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int D);
 int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                 void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int D,
                 int causal, float scale, void* stream);
+
+/*
+ * attn_decode_noalloc - attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. It computes exactly what attn_decode computes, with the same
+ * kernels, and returns bit-identical o and lse.
+ *
+ *   q, k, v, o, lse, B, H, Nq, Nk, D, causal, scale   as in attn_decode.
+ *   stream   a HIP stream (hipStream_t) of the current device, or NULL for its default
+ *            stream; a stream of another device is rejected (ATTN_DECODE_EINVAL).
+ *
+ * Scratch: the per-chunk partials go to a fixed device array of
+ * ATTN_DECODE_NOALLOC_MAX_WORKSPACE bytes inside the library (one per GPU it runs on,
+ * held until the process ends). A call whose attn_decode_workspace_bytes(B, H, Nq, Nk, D)
+ * exceeds it returns ATTN_DECODE_EWORKSPACE before any HIP call; every B*H <= 1024 fits,
+ * whatever Nq (<= 32) and Nk. The first call on a device looks the array's address up
+ * (hipGetSymbolAddress); no call allocates (no hipMalloc, hipFree or allocating library
+ * routine).
+ * Concurrency: all calls on one GPU share that array. Calls that may overlap in time on
+ * one GPU (different streams, or threads without ordering between their launches) race
+ * on it and give wrong results; calls on one stream are ordered and safe.
+ * Errors: as attn_decode (ATTN_DECODE_ELAUNCH also covers a failed address lookup).
+ */
+int attn_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Nq, int Nk, int D, int causal, float scale,
+                        void* stream);
 
 /* attn_decode_strerror - a static, NUL-terminated description of a return code. */
 const char* attn_decode_strerror(int code);

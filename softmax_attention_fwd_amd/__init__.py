@@ -5,9 +5,9 @@
 library is loaded on first use and its absence is an error (there is no fallback path).
 """
 from .binding import (AttnBwdError, AttnDecodeError, AttnFwdError, BasedFwdError, GemmError,
-                      attn_bwd, attn_decode, attn_fwd, based_fwd, bwd_workspace_bytes,
+                      attn_bwd, attn_decode, attn_decode_noalloc, attn_fwd, based_fwd, bwd_workspace_bytes,
                       decode_workspace_bytes, gemm_nt, library_path, load_library)
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "gemm_nt", "based_fwd", "bwd_workspace_bytes",
+__all__ = ["attn_fwd", "attn_bwd", "attn_decode", "attn_decode_noalloc", "gemm_nt", "based_fwd", "bwd_workspace_bytes",
            "decode_workspace_bytes", "library_path", "load_library", "AttnFwdError", "AttnBwdError",
            "AttnDecodeError", "GemmError", "BasedFwdError"]

@@ -16,6 +16,7 @@ C entry points (declared in include/attn_fwd.h, attn_bwd.h, attn_decode.h, tile_
   size_t attn_decode_workspace_bytes(B, H, Nq, Nk, D)
   int attn_decode(q, k, v, o, lse, workspace, workspace_bytes, B, H, Nq, Nk, D, causal,
                   scale, stream)
+  int attn_decode_noalloc(q, k, v, o, lse, B, H, Nq, Nk, D, causal, scale, stream)
   const char* attn_decode_strerror(int code)
   int gemm_bf16_nt(a, b, c, M, N, K, stream)
   const char* gemm_strerror(int code)
@@ -83,6 +84,8 @@ def load_library():
         lib.attn_decode_workspace_bytes.restype = sz
         lib.attn_decode.argtypes = [vp] * 6 + [sz] + [ci] * 6 + [ctypes.c_float, vp]
         lib.attn_decode.restype = ci
+        lib.attn_decode_noalloc.argtypes = [vp] * 5 + [ci] * 6 + [ctypes.c_float, vp]
+        lib.attn_decode_noalloc.restype = ci
         lib.attn_decode_strerror.argtypes = [ci]
         lib.attn_decode_strerror.restype = ctypes.c_char_p
         lib.gemm_bf16_nt.argtypes = [vp, vp, vp, ci, ci, ci, vp]
@@ -291,6 +294,49 @@ def attn_decode(q, k, v, causal: bool = False, scale: float | None = None, out=N
         msg = lib.attn_decode_strerror(code).decode()
         if code in (ATTN_FWD_EINVAL, ATTN_FWD_EUNSUPPORTED, ATTN_FWD_EALIGN, ATTN_BWD_EWORKSPACE):
             raise ValueError(f"attn_decode rejected its arguments (code {code}): {msg}")
+        raise AttnDecodeError(code, msg)
+    return out, lse
+
+
+def attn_decode_noalloc(q, k, v, causal: bool = False, scale: float | None = None, out=None,
+                        lse=None, stream=None):
+    """attn_decode without a workspace: the C entry point keeps the per-chunk partials in a
+    fixed device array of its own (ATTN_DECODE_NOALLOC_MAX_WORKSPACE bytes per GPU), so the
+    library allocates nothing. ``out`` and ``lse`` are allocated here with torch when not
+    given. Calls that overlap in time on one GPU share that array and race."""
+    import torch
+
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(name, t)
+    if k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError(f"shapes do not match: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if len({t.device for t in (q, k, v)}) != 1:
+        raise ValueError("q, k, v must be on the same device")
+    B, H, Nq, D = (int(x) for x in q.shape)
+    Nk = int(k.shape[2])
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_bf16("out", out)
+        if out.shape != q.shape or out.device != q.device:
+            raise ValueError("out must be shaped like q on q's device")
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous()
+          or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, H, Nq] on q's device")
+    lib = load_library()
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        code = lib.attn_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       lse.data_ptr(), B, H, Nq, Nk, D, int(bool(causal)),
+                                       float(scale), handle)
+    if code != ATTN_FWD_OK:
+        msg = lib.attn_decode_strerror(code).decode()
+        if code in (ATTN_FWD_EINVAL, ATTN_FWD_EUNSUPPORTED, ATTN_FWD_EALIGN, ATTN_BWD_EWORKSPACE):
+            raise ValueError(f"attn_decode_noalloc rejected its arguments (code {code}): {msg}")
         raise AttnDecodeError(code, msg)
     return out, lse
 

@@ -24,6 +24,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "attn_decode.h"
 #include "tile_lds.h"
 
@@ -283,22 +286,10 @@ bool sizes_ok(int B, int H, int Nq, int Nk, int D) {
          (int64_t)B * H < ((int64_t)1 << 24) && (int64_t)Nk * D < ((int64_t)1 << 31);
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int D) {
-  if (!sizes_ok(B, H, Nq, Nk, D) || Nq > kMaxQ) return 0;
-  int S, chunk;
-  split_plan(B * H, Nk, &S, &chunk);
-  const size_t rows = (size_t)B * H * S * Nq;
-  return round_up(rows * D * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
-}
-
-int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
-                void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int D,
-                int causal, float scale, void* stream) {
-  if (!q || !k || !v || !o || !lse || !workspace) return ATTN_DECODE_EINVAL;
+// Host-side validation shared by both entry points; makes no HIP call.
+int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               int B, int H, int Nq, int Nk, int D, int causal, float scale) {
+  if (!q || !k || !v || !o || !lse) return ATTN_DECODE_EINVAL;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_DECODE_EINVAL;
   if (causal != 0 && causal != 1) return ATTN_DECODE_EINVAL;
   if (causal && Nq > Nk) return ATTN_DECODE_EINVAL;
@@ -306,11 +297,18 @@ int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse
   if (D != 64 && D != 128) return ATTN_DECODE_EUNSUPPORTED;
   if (Nq > kMaxQ) return ATTN_DECODE_EUNSUPPORTED;
   if (!sizes_ok(B, H, Nq, Nk, D)) return ATTN_DECODE_EINVAL;
-  if (workspace_bytes < attn_decode_workspace_bytes(B, H, Nq, Nk, D)) return ATTN_DECODE_EWORKSPACE;
-  const uintptr_t a16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o;
-  if ((a16 & 15u) != 0 || ((uintptr_t)lse & 3u) != 0 || ((uintptr_t)workspace & 255u) != 0)
-    return ATTN_DECODE_EALIGN;
+  return ATTN_DECODE_OK;
+}
 
+bool aligned(const void* q, const void* k, const void* v, const void* o, const float* lse) {
+  const uintptr_t a16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o;
+  return (a16 & 15u) == 0 && ((uintptr_t)lse & 3u) == 0;
+}
+
+// Split and merge kernels over validated arguments; the partials go to `workspace`, a
+// device address of at least attn_decode_workspace_bytes(...) bytes, 256-byte aligned.
+int launch(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+           int B, int H, int Nq, int Nk, int D, int causal, float scale, void* stream) {
   DecParams p;
   p.q = static_cast<const __bf16*>(q);
   p.k = static_cast<const __bf16*>(k);
@@ -342,6 +340,83 @@ int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse
   return ATTN_DECODE_OK;
 }
 
+// ---- fixed scratch of attn_decode_noalloc
+//
+// The per-chunk partials of attn_decode_noalloc live in this device array instead of a
+// caller workspace. Every GPU the library runs on holds its own copy from the module's
+// load until the process ends. In host code `scratch` names a host-side stand-in, not
+// the device array: its device address is taken once per device with
+// hipGetSymbolAddress (with that device current) and only that address is ever passed
+// to a kernel. The split kernel writes every partial the merge kernel reads, so nothing
+// has to be cleared between calls.
+constexpr size_t kNoAllocScratchBytes = ATTN_DECODE_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The device address of `scratch` on the current device (looked up on the first call on
+// that device). A non-null stream must belong to the current device.
+int noalloc_scratch(void* stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_DECODE_ELAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_DECODE_EUNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = 0;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) return ATTN_DECODE_ELAUNCH;
+    if ((int)sdev != dev) return ATTN_DECODE_EINVAL;
+  }
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return ATTN_DECODE_ELAUNCH;
+      if (((uintptr_t)ptr & 255u) != 0) return ATTN_DECODE_EALIGN;
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return ATTN_DECODE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int D) {
+  if (!sizes_ok(B, H, Nq, Nk, D) || Nq > kMaxQ) return 0;
+  int S, chunk;
+  split_plan(B * H, Nk, &S, &chunk);
+  const size_t rows = (size_t)B * H * S * Nq;
+  return round_up(rows * D * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+}
+
+int attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int D,
+                int causal, float scale, void* stream) {
+  if (!workspace) return ATTN_DECODE_EINVAL;
+  const int rc = check_args(q, k, v, o, lse, B, H, Nq, Nk, D, causal, scale);
+  if (rc != ATTN_DECODE_OK) return rc;
+  if (workspace_bytes < attn_decode_workspace_bytes(B, H, Nq, Nk, D)) return ATTN_DECODE_EWORKSPACE;
+  if (!aligned(q, k, v, o, lse) || ((uintptr_t)workspace & 255u) != 0) return ATTN_DECODE_EALIGN;
+  return launch(q, k, v, o, lse, workspace, B, H, Nq, Nk, D, causal, scale, stream);
+}
+
+int attn_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Nq, int Nk, int D, int causal, float scale,
+                        void* stream) {
+  int rc = check_args(q, k, v, o, lse, B, H, Nq, Nk, D, causal, scale);
+  if (rc != ATTN_DECODE_OK) return rc;
+  if (attn_decode_workspace_bytes(B, H, Nq, Nk, D) > kNoAllocScratchBytes) return ATTN_DECODE_EWORKSPACE;
+  if (!aligned(q, k, v, o, lse)) return ATTN_DECODE_EALIGN;
+  void* ws = nullptr;
+  rc = noalloc_scratch(stream, &ws);
+  if (rc != ATTN_DECODE_OK) return rc;
+  return launch(q, k, v, o, lse, ws, B, H, Nq, Nk, D, causal, scale, stream);
+}
+
 const char* attn_decode_strerror(int code) {
   switch (code) {
     case ATTN_DECODE_OK: return "success";
@@ -349,7 +424,7 @@ const char* attn_decode_strerror(int code) {
     case ATTN_DECODE_EUNSUPPORTED: return "unsupported shape (D must be 64 or 128, Nq at most 32)";
     case ATTN_DECODE_EALIGN: return "misaligned pointer (tensors need 16 bytes, lse 4, workspace 256)";
     case ATTN_DECODE_ELAUNCH: return "kernel launch failed";
-    case ATTN_DECODE_EWORKSPACE: return "workspace smaller than attn_decode_workspace_bytes(...)";
+    case ATTN_DECODE_EWORKSPACE: return "workspace smaller than attn_decode_workspace_bytes(...), or (attn_decode_noalloc) larger than its fixed scratch";
     default: return "unknown error code";
   }
 }

@@ -43,7 +43,7 @@ def declared_codes(prefix="ATTN_FWD_"):
 
 def test_header_declares_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_strerror", "attn_bwd_workspace_bytes",
-                                    "attn_decode", "attn_decode_strerror",
+                                    "attn_decode", "attn_decode_noalloc", "attn_decode_strerror",
                                     "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_strerror"]
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "tile_gemm.h")).read(), flags=re.S)
     assert sorted(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(gemm_\w+)\s*\(", text, flags=re.M)) == \
@@ -211,6 +211,39 @@ def call_dec(lib, q=A, k=A, v=A, o=A, lse=A, ws=W, ws_bytes=1 << 24, B=1, H=1, N
 ])
 def test_decode_invalid_arguments_rejected(lib, kw, code):
     assert call_dec(lib, **kw) == code
+
+
+def call_dec_noalloc(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, Nq=1, Nk=128, D=64, causal=0,
+                     scale=0.125):
+    return lib.attn_decode_noalloc(q, k, v, o, lse, B, H, Nq, Nk, D, causal, ctypes.c_float(scale), None)
+
+
+NOALLOC_MAX = 33 << 20  # ATTN_DECODE_NOALLOC_MAX_WORKSPACE
+
+
+def test_decode_noalloc_limit_declared():
+    text = open(os.path.join(ROOT, "include", "attn_decode.h")).read()
+    m = re.search(r"#define\s+ATTN_DECODE_NOALLOC_MAX_WORKSPACE\s+\(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == NOALLOC_MAX
+
+
+def test_decode_noalloc_limit_covers_up_to_1024_heads(lib):
+    # the chunk plan keeps B*H*S below 1024 + B*H, so 32 queries of D = 128 fit for B*H <= 1024
+    for bh in (1, 7, 256, 1000, 1024):
+        for nk in (1, 129, 4096, 131072, (1 << 24) - 1):
+            assert 0 < lib.attn_decode_workspace_bytes(1, bh, 32, nk, 128) <= NOALLOC_MAX
+    assert lib.attn_decode_workspace_bytes(64, 64, 32, 256, 128) > NOALLOC_MAX
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(lse=None), -1), (dict(Nq=0), -1), (dict(B=0), -1),
+    (dict(causal=2), -1), (dict(causal=1, Nq=8, Nk=4), -1), (dict(scale=-1.0), -1),
+    (dict(D=96), -2), (dict(Nq=33), -2),
+    (dict(B=64, H=64, Nq=32, Nk=256, D=128), -5),   # partials beyond the fixed scratch
+    (dict(q=A + 8), -3), (dict(lse=A + 1), -3),
+])
+def test_decode_noalloc_invalid_arguments_rejected(lib, kw, code):
+    assert call_dec_noalloc(lib, **kw) == code
 
 
 def test_gemm_codes_and_strerror(lib):
