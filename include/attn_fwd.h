@@ -56,10 +56,8 @@ extern "C" {
  * no state between calls, and may be called concurrently from several host threads on
  * different streams. The kernel is chosen by shape: ping-pong for D = 128; for D = 64,
  * ping-pong when causal == 0 and B * H * ceil(N / 256) is at least the compute-unit count
- * of the current device (which the call queries), else four-wave. Both give identical
- * results. Each call reads two testing and tuning variables from the environment:
- * ATTN_FWD_KERNEL=pingpong|fourwave overrides that choice, and ATTN_FWD_BC=32 selects
- * 32-key tiles in the four-wave kernel (default 64).
+ * of the current device (queried once per device), else four-wave. Both give identical
+ * results. The library reads no environment variable.
  *
  * Behaviour: arguments are validated on the host before any HIP call; an invalid call
  * returns a negative code and enqueues nothing. A valid call enqueues one kernel and
@@ -69,6 +67,23 @@ extern "C" {
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int N, int D, int causal, float scale, void* stream);
+
+/* Kernel selectors of attn_fwd_ex. */
+#define ATTN_FWD_KERNEL_AUTO      0   /* attn_fwd's choice by shape                          */
+#define ATTN_FWD_KERNEL_PINGPONG  1   /* 8 waves, 256 queries per workgroup, two wave groups
+                                         alternating matrix and vector phases on each SIMD  */
+#define ATTN_FWD_KERNEL_FOURWAVE  2   /* 4 waves, 128 queries per workgroup, each wave
+                                         interleaving its MFMAs and exponentials            */
+
+/*
+ * attn_fwd_ex - attn_fwd with the kernel chosen by the caller, for tests and tuning. Same
+ * operation, arguments, ownership and behaviour as attn_fwd; kernel is one of the
+ * ATTN_FWD_KERNEL_* selectors (anything else is ATTN_FWD_EINVAL). Both kernels run every
+ * valid shape and perform the same per-row arithmetic in the same order, so they return
+ * bit-identical o and lse.
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int N, int D, int causal, float scale, int kernel, void* stream);
 
 /* attn_fwd_strerror - a static, NUL-terminated description of a return code. */
 const char* attn_fwd_strerror(int code);

@@ -8,6 +8,7 @@ anything itself.
 
 C entry points (declared in include/attn_fwd.h, attn_bwd.h, attn_decode.h, tile_gemm.h):
   int attn_fwd(q, k, v, o, lse, B, H, N, D, causal, scale, stream)
+  int attn_fwd_ex(q, k, v, o, lse, B, H, N, D, causal, scale, kernel, stream)
   const char* attn_fwd_strerror(int code)
   size_t attn_bwd_workspace_bytes(B, H, N)
   int attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
@@ -38,6 +39,9 @@ ATTN_FWD_EUNSUPPORTED = -2
 ATTN_FWD_EALIGN = -3
 ATTN_FWD_ELAUNCH = -4
 ATTN_BWD_EWORKSPACE = -5
+
+# Kernel selectors of attn_fwd_ex (include/attn_fwd.h).
+FWD_KERNELS = {"auto": 0, "pingpong": 1, "fourwave": 2}
 
 _lock = threading.Lock()
 _lib = None
@@ -71,6 +75,8 @@ def load_library():
         ci = ctypes.c_int
         lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, vp]
         lib.attn_fwd.restype = ci
+        lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ctypes.c_float, ci, vp]
+        lib.attn_fwd_ex.restype = ci
         lib.attn_fwd_strerror.argtypes = [ci]
         lib.attn_fwd_strerror.restype = ctypes.c_char_p
         sz = ctypes.c_size_t
@@ -132,13 +138,15 @@ def _check_bf16(name, t):
 
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
-             stream=None):
+             stream=None, kernel: str = "auto"):
     """Fused softmax attention forward on the GPU.
 
     q, k, v: contiguous bfloat16 CUDA tensors of shape [B, H, N, D], D in {64, 128}.
     Returns (O bfloat16 [B, H, N, D], lse float32 [B, H, N]); ``out``/``lse`` may be
     given to write in place. ``scale`` defaults to 1/sqrt(D). The call is asynchronous
     on ``stream`` (a torch.cuda.Stream or raw handle; default: torch's current stream).
+    ``kernel`` "auto" calls attn_fwd; "pingpong" or "fourwave" calls attn_fwd_ex with
+    that kernel forced (tests and tuning; both give identical results).
     """
     import torch
 
@@ -161,10 +169,17 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
     elif (tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()
           or lse.device != q.device):
         raise ValueError("lse must be a contiguous float32 tensor of shape [B, H, N] on q's device")
+    if kernel not in FWD_KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(FWD_KERNELS)}")
     handle = _stream_handle(stream, q.device)
     lib = load_library()
-    code = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                        B, H, N, D, int(bool(causal)), float(scale), handle)
+    if kernel == "auto":
+        code = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            B, H, N, D, int(bool(causal)), float(scale), handle)
+    else:
+        code = lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, H, N, D, int(bool(causal)), float(scale),
+                               FWD_KERNELS[kernel], handle)
     if code != ATTN_FWD_OK:
         msg = lib.attn_fwd_strerror(code).decode()
         if code in (ATTN_FWD_EINVAL, ATTN_FWD_EUNSUPPORTED, ATTN_FWD_EALIGN):

@@ -23,7 +23,7 @@
 //     are already the B operand of that MFMA (8 keys of its query), given that the A
 //     operand (V^T) pairs its k positions with the same 8 keys; V^T fragments come from
 //     LDS through ds_read_b64_tr_b16, which transposes 4x16 bf16 blocks across lanes.
-//   * K and V tiles (64 keys by default, or 32 in the four-wave kernel) are copied
+//   * K and V tiles of 64 keys are copied
 //     global -> LDS by buffer_load ... lds into double-buffered rings; the K ring runs one
 //     tile ahead, so the score MFMAs of tile t+1 overlap the exponentials of tile t. The
 //     16-byte chunks of each tile row are permuted so that the K reads and the transposing
@@ -41,29 +41,22 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
-#include <stdlib.h>
-#include <string.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "attn_fwd.h"
+#include "tile_lds.h"
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) void lds_void;
+using namespace attn_tile;
 
 constexpr int kWaves = 4;
 constexpr int kQW = 32;              // query rows per wave
 constexpr int kBr = kWaves * kQW;    // query rows per workgroup
 constexpr int kWavesPP = 8;          // ping-pong kernel: waves per workgroup
 constexpr int kBrPP = kWavesPP * kQW;  // ping-pong kernel: query rows per workgroup
-constexpr float kLn2 = 0.693147180559945309f;
-constexpr float kLog2e = 1.44269504088896341f;
-constexpr int kWaitVmcnt0 = 0x0F70;    // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold, in log2 units of probability
 
 struct Params {
@@ -84,12 +77,6 @@ __device__ inline float max_across_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Both halves of the wave receive x[lane] + x[lane ^ 32].
-__device__ inline float sum_across_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // LDS tile layout. A K or V tile is BC rows (keys) of D bf16, row-major and unpadded; the
 // 16-byte chunks of each row are permuted: logical chunk c of row r sits at physical chunk
 // c ^ f(r). The LDS has 64 four-byte banks; a 16-byte-per-lane read is serviced 16 lanes
@@ -103,13 +90,7 @@ __device__ inline float sum_across_halves(float x) {
 //    of four consecutive rows, twice; f only has to separate those four rows in the chunk
 //    bits above the two that vary: f = 4(r & 3) for D = 128, 4((r >> 1) & 1) for D = 64.
 // With these choices every read address is a per-lane base (one per K step, one per V
-// column block) plus a compile-time offset.
-template <int D>
-__device__ inline int swz_k(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  const int a = (r >> 1) & 7;
-  return ((a & 1) << 2) | (a >> 1);
-}
+// column block) plus a compile-time offset. The K permutation is attn_tile::swz.
 template <int D>
 __device__ inline int swz_v(int r) {
   if constexpr (D == 128) return (r & 3) << 2;
@@ -155,53 +136,11 @@ __device__ inline void interleave_schedule() {
   }
 }
 
-// Buffer resource over one head's [N, D] bf16 tensor: 64-bit base, no stride, range
-// num_bytes.
-__device__ inline i32x4 make_rsrc(const void* base, uint32_t num_bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xFFFFu));
-  r[2] = __builtin_amdgcn_readfirstlane((int)num_bytes);
-  r[3] = 0x00020000;  // raw 32-bit buffer data format
-  return r;
-}
-
-// One 16-byte-per-lane copy global -> LDS (buffer_load_dwordx4 ... lds): lane l reads
-// rsrc.base + soff + voff[l] and writes LDS address lds + 16*l. The copy is asynchronous
-// (counted by vmcnt); the explicit waits before the barriers complete it. It is issued
-// from inline assembly, without a memory clobber, so that the compiler neither makes
-// unrelated LDS reads wait for it nor treats it as ordered with them: every copy targets
-// a ring slot that no wave reads until after the next barrier, and the reads of that
-// slot's previous contents all precede the barrier before the copy. M0 is used by
-// nothing else in these kernels.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved; see the comment above
-__device__ inline void copy16_to_lds(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, %2 offen lds"
-      :
-      : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
-      : "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ inline void wait_copies_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-}
-
-__device__ inline uint32_t lds_address(const char* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
 template <int D, int BC, int W, bool CAUSAL>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(const Params p) {
   static_assert(D == 64 || D == 128, "head dimension");
-  static_assert(BC == 32 || BC == 64, "key tile");
+  static_assert(BC == 64, "key tile");
   constexpr int kBc = BC;
   constexpr int NB = BC / 32;  // 32-key score blocks per tile
   using L = TileLayout<D, BC, W>;
@@ -216,11 +155,7 @@ void attn_fwd_kernel(const Params p) {
   const int hi = lane >> 5;   // which half of the wave
 
   // ---- work unit: (batch*head, query tile)
-  int g = blockIdx.x;
-  if (p.remap) {
-    const int per_xcd = gridDim.x >> 3;
-    g = (g & 7) * per_xcd + (g >> 3);
-  }
+  const int g = remap_block(blockIdx.x, p.remap);
   const int bh = g / p.n_qtiles;
   int qt = g - bh * p.n_qtiles;
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // longest tiles first
@@ -254,7 +189,7 @@ void attn_fwd_kernel(const Params p) {
 #pragma unroll
   for (int i = 0; i < L::kPeriodK; ++i) {
     const int row = (wave * L::kCopies + i) * L::kRowsPerCopy + lane / L::kChunks;
-    koff[i] = row * RB + (((lane % L::kChunks) ^ swz_k<D>(row)) << 4);
+    koff[i] = row * RB + (((lane % L::kChunks) ^ swz<D>(row)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < L::kPeriodV; ++i) {
@@ -308,7 +243,7 @@ void attn_fwd_kernel(const Params p) {
   // 32j + m; the permutation depends on m only, so k_addr[st] covers every j and buffer.
   int k_addr[D / 16];
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) k_addr[st] = col * RB + 16 * ((2 * st + hi) ^ swz_k<D>(col));
+  for (int st = 0; st < D / 16; ++st) k_addr[st] = col * RB + 16 * ((2 * st + hi) ^ swz<D>(col));
   // V^T (A operand of O^T = V^T P^T) through ds_read_b64_tr_b16: in each 16-lane group
   // the source lane jj supplies 8 bytes of row 16st + 8u + 4h + (jj >> 2) at logical column
   // 32d + 16(grp & 1) + 4(jj & 3); the instruction hands lane jj column jj of that 4-row
@@ -547,11 +482,7 @@ void attn_fwd_pp_kernel(const Params p) {
   const int col = lane & 31;
   const int hi = lane >> 5;
 
-  int g = blockIdx.x;
-  if (p.remap) {
-    const int per_xcd = gridDim.x >> 3;
-    g = (g & 7) * per_xcd + (g >> 3);
-  }
+  const int g = remap_block(blockIdx.x, p.remap);
   const int bh = g / p.n_qtiles;
   int qt = g - bh * p.n_qtiles;
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;
@@ -580,7 +511,7 @@ void attn_fwd_pp_kernel(const Params p) {
 #pragma unroll
   for (int i = 0; i < LC::kPeriodK; ++i) {
     const int row = (cw * LC::kCopies + i) * LC::kRowsPerCopy + lane / LC::kChunks;
-    koff[i] = row * RB + (((lane % LC::kChunks) ^ swz_k<D>(row)) << 4);
+    koff[i] = row * RB + (((lane % LC::kChunks) ^ swz<D>(row)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < LC::kPeriodV; ++i) {
@@ -628,7 +559,7 @@ void attn_fwd_pp_kernel(const Params p) {
 
   int k_addr[D / 16];
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) k_addr[st] = col * RB + 16 * ((2 * st + hi) ^ swz_k<D>(col));
+  for (int st = 0; st < D / 16; ++st) k_addr[st] = col * RB + 16 * ((2 * st + hi) ^ swz<D>(col));
   const int jj = lane & 15;
   const int gq = lane >> 4;
   int v_addr[D / 32];
@@ -854,37 +785,37 @@ void attn_fwd_pp_kernel(const Params p) {
   }
 }
 
-template <int D, int BC, int W>
-void launch(int causal, dim3 grid, hipStream_t s, const Params& p) {
-  const dim3 block(64 * W);
-  if (causal) hipLaunchKernelGGL((attn_fwd_kernel<D, BC, W, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((attn_fwd_kernel<D, BC, W, false>), grid, block, 0, s, p);
-}
-
 // Kernel choice. D = 128 runs the ping-pong kernel. D = 64 runs the ping-pong kernel when
 // the mask is off and its grid (one workgroup of 256 queries per compute unit) fills the
 // device, else the four-wave kernel. At D = 64 a vector phase costs as much as at D = 128
 // while a matrix phase halves; measured on MI355X (interleaved, 200 launches each), the
 // ping-pong kernel is still 3-7% faster non-causal (B16 H16 N1024 to B1 H32 N4096), but
 // 10% slower causal, where the waves of a workgroup stop at different diagonal tiles, and
-// slower on grids that leave compute units idle (B1 H4 N8192: 570 vs 630 TFLOP/s). Two
-// environment variables, read at every call so that tests can exercise each path in one
-// process, override the choice for testing and tuning: ATTN_FWD_KERNEL=pingpong|fourwave,
-// and ATTN_FWD_BC=32|64 for the key tile of the four-wave kernel.
-enum class Kernel { kPingPong, kFourWave };
-
-Kernel choose_kernel(int D, int64_t pp_grid, int causal, int cus) {
-  const char* e = getenv("ATTN_FWD_KERNEL");
-  if (e && strcmp(e, "pingpong") == 0) return Kernel::kPingPong;
-  if (e && strcmp(e, "fourwave") == 0) return Kernel::kFourWave;
-  if (D == 128) return Kernel::kPingPong;
-  return (!causal && pp_grid >= cus) ? Kernel::kPingPong : Kernel::kFourWave;
+// slower on grids that leave compute units idle (B1 H4 N8192: 570 vs 630 TFLOP/s).
+// attn_fwd_ex can force either kernel, for tests and tuning.
+bool use_pingpong(int D, int64_t pp_grid, int causal, int cus) {
+  if (D == 128) return true;
+  return !causal && pp_grid >= cus;
 }
 
-int key_tile() {
-  const char* e = getenv("ATTN_FWD_BC");
-  const int v = e ? atoi(e) : 0;
-  return (v == 32) ? 32 : 64;
+// Compute units per device, queried once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+std::mutex g_cus_mutex;
+
+int device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_FWD_ELAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_FWD_ELAUNCH;
+  int n = g_cus[dev].load(std::memory_order_acquire);
+  if (n == 0) {
+    std::lock_guard<std::mutex> lock(g_cus_mutex);
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return ATTN_FWD_ELAUNCH;
+    g_cus[dev].store(n, std::memory_order_release);
+  }
+  *cus = n;
+  return ATTN_FWD_OK;
 }
 
 }  // namespace
@@ -902,12 +833,15 @@ const char* attn_fwd_strerror(int code) {
   }
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-             int N, int D, int causal, float scale, void* stream) {
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int N, int D, int causal, float scale, int kernel, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_FWD_EINVAL;
   if (B < 1 || H < 1 || N < 1) return ATTN_FWD_EINVAL;
   if (causal != 0 && causal != 1) return ATTN_FWD_EINVAL;
   if (!(scale > 0.f) || !isfinite(scale)) return ATTN_FWD_EINVAL;
+  if (kernel != ATTN_FWD_KERNEL_AUTO && kernel != ATTN_FWD_KERNEL_PINGPONG &&
+      kernel != ATTN_FWD_KERNEL_FOURWAVE)
+    return ATTN_FWD_EINVAL;
   if (D != 64 && D != 128) return ATTN_FWD_EUNSUPPORTED;
   const int64_t n_qtiles = ((int64_t)N + kBr - 1) / kBr;
   const int64_t grid = (int64_t)B * H * n_qtiles;
@@ -929,14 +863,16 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t n_qtiles_pp = ((int64_t)N + kBrPP - 1) / kBrPP;
   const int64_t grid_pp = (int64_t)B * H * n_qtiles_pp;
-  int cus = 0;
-  if (D == 64 && !causal) {  // the compute units of the current device decide the D = 64 kernel
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return ATTN_FWD_ELAUNCH;
+  bool pingpong = kernel == ATTN_FWD_KERNEL_PINGPONG;
+  if (kernel == ATTN_FWD_KERNEL_AUTO) {
+    int cus = 0;
+    if (D == 64 && !causal) {  // the compute units of the current device decide the D = 64 kernel
+      const int rc = device_cus(&cus);
+      if (rc != ATTN_FWD_OK) return rc;
+    }
+    pingpong = use_pingpong(D, grid_pp, causal, cus);
   }
-  if (choose_kernel(D, grid_pp, causal, cus) == Kernel::kPingPong) {
+  if (pingpong) {
     p.n_qtiles = (int)n_qtiles_pp;
     p.remap = (grid_pp % 8 == 0) ? 1 : 0;
     const dim3 gpp((unsigned)grid_pp), bpp(64 * kWavesPP);
@@ -948,18 +884,22 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
       else hipLaunchKernelGGL((attn_fwd_pp_kernel<128, 64, false>), gpp, bpp, 0, s, p);
     }
   } else {
-    const dim3 grid_dim((unsigned)grid);
-    const int bc = key_tile();
+    const dim3 grid_dim((unsigned)grid), block(64 * kWaves);
     if (D == 64) {
-      if (bc == 32) launch<64, 32, kWaves>(causal, grid_dim, s, p);
-      else launch<64, 64, kWaves>(causal, grid_dim, s, p);
+      if (causal) hipLaunchKernelGGL((attn_fwd_kernel<64, 64, kWaves, true>), grid_dim, block, 0, s, p);
+      else hipLaunchKernelGGL((attn_fwd_kernel<64, 64, kWaves, false>), grid_dim, block, 0, s, p);
     } else {
-      if (bc == 32) launch<128, 32, kWaves>(causal, grid_dim, s, p);
-      else launch<128, 64, kWaves>(causal, grid_dim, s, p);
+      if (causal) hipLaunchKernelGGL((attn_fwd_kernel<128, 64, kWaves, true>), grid_dim, block, 0, s, p);
+      else hipLaunchKernelGGL((attn_fwd_kernel<128, 64, kWaves, false>), grid_dim, block, 0, s, p);
     }
   }
   if (hipGetLastError() != hipSuccess) return ATTN_FWD_ELAUNCH;
   return ATTN_FWD_OK;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int N, int D, int causal, float scale, void* stream) {
+  return attn_fwd_ex(q, k, v, o, lse, B, H, N, D, causal, scale, ATTN_FWD_KERNEL_AUTO, stream);
 }
 
 }  // extern "C"

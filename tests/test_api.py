@@ -44,7 +44,8 @@ def declared_codes(prefix="ATTN_FWD_"):
 def test_header_declares_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_strerror", "attn_bwd_workspace_bytes",
                                     "attn_decode", "attn_decode_noalloc", "attn_decode_strerror",
-                                    "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_strerror"]
+                                    "attn_decode_workspace_bytes", "attn_fwd", "attn_fwd_ex",
+                                    "attn_fwd_strerror"]
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "tile_gemm.h")).read(), flags=re.S)
     assert sorted(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(gemm_\w+)\s*\(", text, flags=re.M)) == \
         ["gemm_bf16_nt", "gemm_strerror"]
@@ -62,8 +63,13 @@ def test_exports_every_declared_symbol(lib):
         assert name in exported
 
 
+def test_kernel_selectors_match_binding():
+    assert declared_codes("ATTN_FWD_KERNEL_") == {
+        "ATTN_FWD_KERNEL_" + k.upper(): v for k, v in binding.FWD_KERNELS.items()}
+
+
 def test_codes_match_binding():
-    codes = declared_codes()
+    codes = {k: v for k, v in declared_codes().items() if not k.startswith("ATTN_FWD_KERNEL_")}
     assert codes == {
         "ATTN_FWD_OK": binding.ATTN_FWD_OK,
         "ATTN_FWD_EINVAL": binding.ATTN_FWD_EINVAL,
@@ -89,11 +95,12 @@ def test_bwd_strerror(lib):
 
 def test_strerror(lib):
     seen = set()
-    for code in declared_codes().values():
+    codes = {k: v for k, v in declared_codes().items() if not k.startswith("ATTN_FWD_KERNEL_")}
+    for code in codes.values():
         msg = lib.attn_fwd_strerror(code).decode()
         assert msg and msg != "unknown error code"
         seen.add(msg)
-    assert len(seen) == len(declared_codes())
+    assert len(seen) == len(codes)
     assert lib.attn_fwd_strerror(12345).decode() == "unknown error code"
 
 
@@ -120,6 +127,13 @@ def call(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=128, D=64, causal=0, scale=
 ])
 def test_invalid_arguments_rejected(lib, kw, code):
     assert call(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kernel,code", [(3, -1), (-1, -1), (1, -2), (2, -2)])
+def test_fwd_ex_rejects_bad_kernel_and_shape(lib, kernel, code):
+    # an unknown selector is EINVAL; a valid one still validates the rest (D = 96 here)
+    D = 96 if code == -2 else 64
+    assert lib.attn_fwd_ex(A, A, A, A, A, 1, 1, 128, D, 0, ctypes.c_float(0.125), kernel, None) == code
 
 
 def test_binding_rejects_cpu_and_bad_dtypes():

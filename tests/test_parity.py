@@ -91,11 +91,11 @@ def test_small_shapes_full_oracle(B, H, N, D, causal, sigma):
 
 
 # Both forward kernels (ping-pong, the D = 128 default and the non-causal D = 64 default on
-# grids that fill the device, and four-wave, the other D = 64 default) are selectable per
-# call through ATTN_FWD_KERNEL. They perform the same per-row arithmetic
-# in the same order, so their outputs must agree bit for bit; each is also held to the
-# oracle on the non-default head dimension. The shapes include grids of more workgroups
-# than the GPU holds at once.
+# grids that fill the device, and four-wave, the other D = 64 default) can be forced per
+# call through attn_fwd_ex. They perform the same per-row arithmetic in the same order,
+# so their outputs must agree bit for bit; each is also held to the oracle on the
+# non-default head dimension. The shapes include grids of more workgroups than the GPU
+# holds at once.
 KERNEL_PAIRS = [
     # B, H, N, D, causal
     (1, 1, 1, 64, False), (1, 2, 17, 128, True), (2, 1, 300, 64, True),
@@ -108,15 +108,9 @@ KERNEL_PAIRS = [
 
 @pytest.mark.parametrize("B,H,N,D,causal", KERNEL_PAIRS,
                          ids=[f"B{b}H{h}N{n}D{d}{'c' if c else 'n'}" for b, h, n, d, c in KERNEL_PAIRS])
-def test_kernels_bit_identical(B, H, N, D, causal, monkeypatch):
-    if os.environ.get("ATTN_FWD_BC") == "32":
-        pytest.skip("the four-wave kernel with 32-key tiles sums in another order")
+def test_kernels_bit_identical(B, H, N, D, causal):
     q, k, v = (t.cuda() for t in make_qkv(B, H, N, D, seed=11 * N + D))
-    out = {}
-    for kernel in ("pingpong", "fourwave"):
-        monkeypatch.setenv("ATTN_FWD_KERNEL", kernel)
-        out[kernel] = run(q, k, v, causal)
-    monkeypatch.delenv("ATTN_FWD_KERNEL")
+    out = {kernel: run(q, k, v, causal, kernel=kernel) for kernel in ("pingpong", "fourwave")}
     default = run(q, k, v, causal)
     (o_p, l_p), (o_f, l_f) = out["pingpong"], out["fourwave"]
     assert torch.equal(o_p, o_f), f"O differs: max {(o_p.float() - o_f.float()).abs().max().item()}"
@@ -137,10 +131,9 @@ def test_many_workgroups_full_oracle(B, H, N):
 
 @pytest.mark.parametrize("kernel,D", [("pingpong", 64), ("fourwave", 128)])
 @pytest.mark.parametrize("N,causal", [(1, False), (129, True), (1000, False), (2048, True)])
-def test_non_default_kernel_full_oracle(kernel, D, N, causal, monkeypatch):
-    monkeypatch.setenv("ATTN_FWD_KERNEL", kernel)
+def test_non_default_kernel_full_oracle(kernel, D, N, causal):
     q, k, v = make_qkv(2, 3, N, D, seed=13 * N + D)
-    o, lse = run(q, k, v, causal)
+    o, lse = run(q, k, v, causal, kernel=kernel)
     o_ref, lse_ref = oracle.attention_fwd(f64(q), f64(k), f64(v), causal, 1 / math.sqrt(D))
     check(o, lse, o_ref, lse_ref, f"{kernel} N{N} D{D} causal={causal}")
 
