@@ -33,7 +33,7 @@ extern "C" {
 #define ATTN_BWD_OK            0   /* success: the kernels were enqueued on the stream       */
 #define ATTN_BWD_EINVAL       -1   /* NULL pointer; B, H or N < 1; causal not 0/1; scale not
                                       finite or <= 0; sizes that overflow the kernels'
-                                      indexing (N*D >= 2^31, B*H*ceil(N/128) >= 2^31
+                                      indexing (N*D >= 2^31, B*H*ceil(N/64) >= 2^31
                                       workgroups, or B*H*N*D/8 >= 2^31)                     */
 #define ATTN_BWD_EUNSUPPORTED -2   /* head dimension D other than 64 or 128                  */
 #define ATTN_BWD_EALIGN       -3   /* a tensor not 16-byte aligned, lse not 4-byte, or the

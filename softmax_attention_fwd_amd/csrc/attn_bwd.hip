@@ -13,24 +13,32 @@
 //   * delta: -Delta_i and -lse_i / scale per row, into the caller's workspace; they
 //     seed the dP and S accumulators, so the MFMAs produce dP - Delta and
 //     s - lse / scale directly (P = exp2(c (s - lse / scale)), c = scale * log2 e).
-//   * dkdv: one workgroup per 128 keys (32 per wave). K and V stay in registers as MFMA
-//     operands; Q and dO stream through LDS in tiles of 64 queries. Per 32 queries and
-//     32 keys: S = Q K^T and dP = dO V^T (v_mfma_f32_32x32x16_bf16, each lane then holds
-//     one key and 16 queries), P and dS in registers, and dV^T += dO^T P,
-//     dK^T += Q^T dS with dO^T / Q^T read transposed from LDS (ds_read_b64_tr_b16) and
-//     P / dS straight from the score registers as the B operand (the MFMA's k order only
-//     has to agree between its operands).
+//   * dkdv (D = 128): one workgroup per 128 keys, 8 waves in pairs of two roles over 32
+//     keys each.
+//     The P wave holds K and the dS wave V in registers as MFMA operands; Q and dO stream
+//     through LDS in tiles of 64 queries. Per 32 queries and 32 keys: S = Q K^T (P wave)
+//     and dP = dO V^T (dS wave) (v_mfma_f32_32x32x16_bf16, each lane then holds one key
+//     and 16 queries), P (P wave, passed to the dS wave through LDS) and dS in registers,
+//     and dV^T += dO^T P (P wave), dK^T += Q^T dS (dS wave) with dO^T / Q^T read
+//     transposed from LDS (ds_read_b64_tr_b16) and P / dS straight from the score
+//     registers as the B operand (the MFMA's k order only has to agree between its
+//     operands). S and dP are formed once here. At D = 64 one wave holds both K and V
+//     and does both roles (dkdv1).
 //   * dq: one workgroup per 128 queries (32 per wave), the forward's shape. Q and dO stay
 //     in registers; K and V stream through LDS in tiles of 64 keys. Per 32 keys:
 //     S^T = K Q^T and dP^T = V dO^T (each lane one query, 16 keys), dS^T, and
 //     dQ^T += K^T dS^T with K^T read transposed.
-// No atomics: every output element is owned by one wave. dQ, dK, dV are written in bf16
-// (round to nearest even) after scaling in fp32.
+// The five N x N x D products run once each plus S and dP again in dq: 14 N^2 D of
+// executed MFMA work for the algorithmic 10 N^2 D. No atomics: every output element is
+// owned by one wave, so the results are the same on every call. dQ, dK, dV are written
+// in bf16 (round to nearest even) after scaling in fp32.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "attn_bwd.h"
 #include "tile_lds.h"
@@ -43,6 +51,7 @@ constexpr int kWaves = 4;
 constexpr int kBlk = 32;            // keys (dkdv) or queries (dq) per wave
 constexpr int kWgRows = kWaves * kBlk;
 constexpr int kTile = 64;           // streamed rows per LDS tile
+constexpr int kPairs = 4;           // dkdv: wave pairs (two roles over the same keys)
 
 struct BwdParams {
   const __bf16* q;
@@ -58,6 +67,8 @@ struct BwdParams {
   __bf16* dv;
   int N;
   int n_wg_tiles;  // ceil(N / kWgRows)
+  int n_kv_tiles;  // ceil(N / (32 kPairs)): dkdv workgroups per head
+  int remap_kv;    // dkdv grid is a multiple of 8: XCD-aware order
   int rows;        // B * H * N
   int remap;       // grid is a multiple of 8: XCD-aware order
   float c;         // scale * log2(e)
@@ -86,17 +97,198 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const BwdParams p) 
   }
 }
 
-// ---- dkdv: workgroup = 128 keys, wave = 32 keys; query tiles of 64 stream through LDS.
-// PART selects the outputs: kDkDv both; kDvOnly dV (no dP, dS or V operand); kDkOnly dK.
-// Both at once need 32 + 32 registers of K and V operands and 64 + 64 of accumulators at
-// D = 128, which leaves too few of a wave's 256 (two waves per SIMD) for the rest, so
-// D = 128 runs the two parts as two kernels (S is formed in both) and D = 64 runs one.
-constexpr int kDkDv = 0, kDvOnly = 1, kDkOnly = 2;
-template <int D, bool CAUSAL, int PART>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// ---- dkdv: kPairs pairs of waves (128 keys a workgroup), each pair on 32 keys in two
+// roles: the P wave (waves 0-3) forms S = Q K^T, P, and dV^T += dO^T P; the dS wave
+// (waves 4-7) forms dP - Delta = dO V^T - Delta, takes P from the P wave through LDS, and
+// accumulates dK^T += Q^T dS. Query tiles of 64 stream through LDS (two slots). Each role
+// holds one of K, V (32 registers at D = 128) and one accumulator (64), so S and dP are
+// formed once without the 128 + 128 registers of both in one wave; the two waves of a
+// SIMD share its MFMAs. Per tile: phase 1 forms S and P (P waves) and dP (dS waves);
+// after a barrier, phase 2 forms dS (dS waves) and adds both products.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(128 * kPairs) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(const BwdParams p) {
-  constexpr bool kDv = PART != kDkOnly;
-  constexpr bool kDk = PART != kDvOnly;
+  static_assert(D == 128, "the two-role kernel serves D = 128");
+  constexpr int RB = 2 * D;
+  constexpr int kWaves2 = 2 * kPairs;
+  constexpr int kKeys = kPairs * kBlk;                   // keys of the workgroup
+  constexpr int kTileBytes = kTile * RB;
+  constexpr int kSlot = 2 * kTileBytes + 2 * kTile * 4;  // Q, dO, -lse/scale, -Delta
+  constexpr int kPBlock = kBlk * kBlk * 2;                // P of one block (bf16)
+  constexpr int kPBytes = (kTile / kBlk) * kPBlock;        // of one pair, one tile
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kSlot + kPairs * kPBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool pw = wave < kPairs;  // P wave (else dS wave)
+  const int pair = wave % kPairs;
+  const int col = lane & 31;
+  const int hi = lane >> 5;
+  const int N = p.N;
+
+  const int g = remap_block(blockIdx.x, p.remap_kv);
+  const int bh = g / p.n_kv_tiles;
+  const int kt = g - bh * p.n_kv_tiles;
+  const size_t head = (size_t)bh * N * D;
+  const int k0 = kt * kKeys + pair * kBlk;  // first key of this pair
+  const int key = k0 + col;
+
+  // K (P waves) or V (dS waves) as B operands (lane = key, k = D index 16st + 8h .. +7)
+  bf16x8 xf[D / 16];
+  {
+    const int r = min(key, N - 1);
+    const bf16x8* src = reinterpret_cast<const bf16x8*>((pw ? p.k : p.v) + head + (size_t)r * D) + hi;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) xf[s] = src[2 * s];
+  }
+  f32x16 acc[D / 32];  // dV^T (P waves) or dK^T (dS waves)
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) acc[d] = f32x16{};
+
+  const uint32_t head_bytes = (uint32_t)N * RB;
+  const i32x4 qrsrc = make_rsrc(p.q + head, head_bytes);
+  const i32x4 orsrc = make_rsrc(p.dout + head, head_bytes);
+  const i32x4 lrsrc = make_rsrc(p.nls + (size_t)bh * N, (uint32_t)N * 4u);
+  const i32x4 drsrc = make_rsrc(p.ndelta + (size_t)bh * N, (uint32_t)N * 4u);
+  const uint32_t smem_lds = lds_address(smem);
+
+  // query tiles: causal workgroups start at their first key
+  const int qt_first = CAUSAL ? (kt * kKeys) / kTile : 0;
+  const int qt_end = (N + kTile - 1) / kTile;
+  auto load = [&](int qt, int slot) {
+    const uint32_t base = smem_lds + slot * kSlot;
+    copy_tile<D, kTile, kWaves2>(qrsrc, qt * kTile, N, base, wave, lane);
+    copy_tile<D, kTile, kWaves2>(orsrc, qt * kTile, N, base + kTileBytes, wave, lane);
+    if (wave == 0) copy_vec64(lrsrc, qt * kTile, N, base + 2 * kTileBytes, lane);
+    if (wave == 1) copy_vec64(drsrc, qt * kTile, N, base + 2 * kTileBytes + kTile * 4, lane);
+  };
+
+  const int rbase = row_read_base<D>(col, hi);
+  int ta[D / 32][2];
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d) {
+    ta[d][0] = tr_read_addr<D>(lane, d, 0);
+    ta[d][1] = tr_read_addr<D>(lane, d, 1);
+  }
+  // this pair's P: block b, half u at pbase + b * kPBlock + u * 1024 + 16 * lane
+  const int pbase = 2 * kSlot + pair * kPBytes + 16 * lane;
+
+  // The two roles run separate loops (compile-time PW) with the same barriers: two a
+  // tile. Every block of a tile is computed; the causal and ragged masks zero P (so dS
+  // too) where a key is not visible, which also covers keys >= N and queries >= N (their
+  // rows are clamped copies, finite).
+  auto role = [&](auto pw_tag) {
+    constexpr bool PW = decltype(pw_tag)::value;
+    f32x16 x[2];      // S - lse / scale (P waves) or dP - Delta (dS waves), per block
+    bf16x8 fr[2][2];  // P (P waves) or dS (dS waves) as B operands, per block and k-step
+    // the first product of both blocks from the tile in slot `sl`: rows of Q (P waves) or
+    // dO (dS waves) times xf, seeded with -lse / scale or -Delta
+    auto first_product = [&](int sl) {
+      const int qs = sl * kSlot;
+      const int xs = PW ? qs : qs + kTileBytes;
+      const int is = qs + 2 * kTileBytes + (PW ? 0 : kTile * 4);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(smem + is + (b * kBlk + 8 * g4 + 4 * hi) * 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[b][4 * g4 + i] = a[i];
+        }
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const bf16x8 ra = *reinterpret_cast<const bf16x8*>(smem + xs + b * kBlk * RB + row_read_addr(rbase, st));
+          x[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra, xf[st], x[b], 0, 0, 0);
+        }
+    };
+    // the second product: acc += (dO or Q of slot `sl`, transposed) fr
+    auto second_product = [&](int sl) {
+      const int ys = sl * kSlot + (PW ? kTileBytes : 0);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int d = 0; d < D / 32; ++d) {
+            const bf16x8 ya = tr_frag<D>(smem, ys, ta[d], b * kBlk + 16 * st);
+            acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ya, fr[b][st], acc[d], 0, 0, 0);
+          }
+    };
+    // P = exp2(c x), masked (MASK) to keys <= query (causal), key < N and query < N; to
+    // fr and to LDS
+    auto make_p = [&](auto mask_tag, int qt) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int qb0 = qt * kTile + b * kBlk;
+        // query index minus this lane's offset 4h, against the limits
+        const int lo_lim = CAUSAL ? key - qb0 - 4 * hi : -1;  // query offset >= lo_lim
+        const int hi_lim = key < N ? N - qb0 - 4 * hi : -1;    // query offset < hi_lim
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = __builtin_amdgcn_exp2f(x[b][r] * p.c);
+          if (MASK) {
+            const int qo = 8 * (r >> 2) + (r & 3);
+            if (qo < lo_lim || qo >= hi_lim) pr = 0.f;
+          }
+          fr[b][r >> 3][r & 7] = (__bf16)pr;
+        }
+        *reinterpret_cast<bf16x8*>(smem + pbase + b * kPBlock) = fr[b][0];
+        *reinterpret_cast<bf16x8*>(smem + pbase + b * kPBlock + 1024) = fr[b][1];
+      }
+    };
+    // dS = P (dP - Delta), P from the P wave through LDS
+    auto make_ds = [&]() {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 pv = *reinterpret_cast<const bf16x8*>(smem + pbase + b * kPBlock + u * 1024);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) fr[b][u][i] = (__bf16)((float)pv[i] * x[b][8 * u + i]);
+        }
+    };
+
+    for (int qt = qt_first; qt < qt_end; ++qt) {
+      const int sl = (qt - qt_first) & 1;
+      wait_copies_and_barrier();
+      if (qt + 1 < qt_end) load(qt + 1, sl ^ 1);
+      first_product(sl);
+      if constexpr (PW) {
+        // every query of the tile sees every key of the pair, all in range
+        const bool plain = (!CAUSAL || qt * kTile >= k0 + kBlk - 1) &&
+                           qt * kTile + kTile <= N && k0 + kBlk <= N;
+        if (plain) make_p(std::false_type{}, qt);
+        else make_p(std::true_type{}, qt);
+      }
+      __syncthreads();
+      if constexpr (!PW) make_ds();
+      second_product(sl);
+    }
+  };
+  if (qt_first < qt_end) load(qt_first, 0);
+  if (pw) role(std::true_type{});
+  else role(std::false_type{});
+  if (key < N) {
+    if (pw) store_rows<D>(p.dv + head + (size_t)key * D, acc, hi, 1.f);
+    else store_rows<D>(p.dk + head + (size_t)key * D, acc, hi, p.scale);
+  }
+}
+
+// ---- dkdv at D = 64: workgroup = 128 keys, wave = 32 keys holding both K and V (16 + 16
+// registers) and both accumulators (32 + 32); query tiles of 64 stream through LDS. At
+// D = 128 the same layout leaves too few of a wave's 256 registers for two waves per SIMD,
+// hence the two-role kernel above; at D = 64 this one is the faster (its 16 MFMAs per
+// block need no barrier in the middle of a tile).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv1_kernel(const BwdParams p) {
+  static_assert(D == 64, "one wave holds both K and V only at D = 64");
+  constexpr bool kDv = true;
+  constexpr bool kDk = true;
   constexpr int RB = 2 * D;
   constexpr int kTileBytes = kTile * RB;
   constexpr int kSlot = 2 * kTileBytes + 2 * kTile * 4;  // Q, dO, -lse/scale, -Delta
@@ -352,23 +544,16 @@ void launch_bwd(int causal, int B, int H, hipStream_t s, const BwdParams& p) {
   hipLaunchKernelGGL(attn_bwd_delta_kernel<D>, dim3((p.rows + rows_per_block - 1) / rows_per_block),
                      block, 0, s, p);
   const dim3 grid((unsigned)(B * H * p.n_wg_tiles));
-  if (causal) {
-    if constexpr (D == 64) {
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, kDkDv>), grid, block, 0, s, p);
-    } else {
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, kDvOnly>), grid, block, 0, s, p);
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true, kDkOnly>), grid, block, 0, s, p);
-    }
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), grid, block, 0, s, p);
+  const dim3 grid_kv((unsigned)(B * H * p.n_kv_tiles));
+  if constexpr (D == 64) {
+    if (causal) hipLaunchKernelGGL((attn_bwd_dkdv1_kernel<D, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((attn_bwd_dkdv1_kernel<D, false>), grid, block, 0, s, p);
   } else {
-    if constexpr (D == 64) {
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, kDkDv>), grid, block, 0, s, p);
-    } else {
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, kDvOnly>), grid, block, 0, s, p);
-      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false, kDkOnly>), grid, block, 0, s, p);
-    }
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), grid, block, 0, s, p);
+    if (causal) hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, true>), grid_kv, dim3(128 * kPairs), 0, s, p);
+    else hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, false>), grid_kv, dim3(128 * kPairs), 0, s, p);
   }
+  if (causal) hipLaunchKernelGGL((attn_bwd_dq_kernel<D, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((attn_bwd_dq_kernel<D, false>), grid, block, 0, s, p);
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -394,8 +579,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (D != 64 && D != 128) return ATTN_BWD_EUNSUPPORTED;
   const int64_t n_tiles = ((int64_t)N + kWgRows - 1) / kWgRows;
   const int64_t grid = (int64_t)B * H * n_tiles;
+  const int64_t grid_kv = (int64_t)B * H * (((int64_t)N + 32 * kPairs - 1) / (32 * kPairs));
   const int64_t rows = (int64_t)B * H * N;
-  if ((int64_t)N * D >= ((int64_t)1 << 31) || grid >= ((int64_t)1 << 31) ||
+  if ((int64_t)N * D >= ((int64_t)1 << 31) || grid_kv >= ((int64_t)1 << 31) ||
       rows * (D / 8) >= ((int64_t)1 << 31))
     return ATTN_BWD_EINVAL;
   if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N)) return ATTN_BWD_EWORKSPACE;
@@ -421,6 +607,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   p.n_wg_tiles = (int)n_tiles;
   p.rows = (int)rows;
   p.remap = (grid % 8 == 0) ? 1 : 0;
+  p.n_kv_tiles = (N + 32 * kPairs - 1) / (32 * kPairs);
+  p.remap_kv = ((int64_t)B * H * p.n_kv_tiles % 8 == 0) ? 1 : 0;
   p.c = scale * kLog2e;
   p.scale = scale;
 
