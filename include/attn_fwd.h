@@ -55,7 +55,7 @@ extern "C" {
  * Ownership: the caller owns every buffer. The library allocates no device memory, keeps
  * no state between calls, and may be called concurrently from several host threads on
  * different streams. The kernel is chosen by shape: ping-pong for D = 128; for D = 64,
- * ping-pong when causal == 0 and B * H * ceil(N / 256) is at least the compute-unit count
+ * ping-pong when causal == 0 and B * H * ceil(N / 512) is at least the compute-unit count
  * of the current device (queried once per device), else four-wave. Both give identical
  * results. The library reads no environment variable.
  *
@@ -70,8 +70,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /* Kernel selectors of attn_fwd_ex. */
 #define ATTN_FWD_KERNEL_AUTO      0   /* attn_fwd's choice by shape                          */
-#define ATTN_FWD_KERNEL_PINGPONG  1   /* 8 waves, 256 queries per workgroup, two wave groups
-                                         alternating matrix and vector phases on each SIMD  */
+#define ATTN_FWD_KERNEL_PINGPONG  1   /* 8 waves, 256 queries per workgroup (512 at D = 64
+                                         without the mask), two wave groups alternating
+                                         matrix and vector phases on each SIMD              */
 #define ATTN_FWD_KERNEL_FOURWAVE  2   /* 4 waves, 128 queries per workgroup, each wave
                                          interleaving its MFMAs and exponentials            */
 

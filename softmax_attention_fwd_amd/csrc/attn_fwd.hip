@@ -10,10 +10,11 @@
 // those pages; they follow the usual FlashAttention conventions.
 //
 // gfx950 design (not the H100 one):
-//   * each wave owns 32 query rows. Two kernels share the per-row arithmetic below and give
-//     identical results: the ping-pong kernel (8 waves, 256 queries per workgroup, one
-//     workgroup per compute unit, two wave groups alternating matrix and vector phases on
-//     every SIMD), used at D = 128 and for non-causal D = 64 on grids that fill the device;
+//   * each wave owns 32 query rows (64 in the non-causal D = 64 ping-pong kernel). Two
+//     kernels share the per-row arithmetic below and give identical results: the ping-pong
+//     kernel (8 waves, 256 queries per workgroup, 512 at non-causal D = 64; one workgroup
+//     per compute unit, two wave groups alternating matrix and vector phases on every
+//     SIMD), used at D = 128 and for non-causal D = 64 on grids that fill the device;
 //     and the four-wave kernel (128 queries per workgroup, two workgroups per compute
 //     unit, each wave interleaving its own MFMAs and exponentials), used otherwise.
 //   * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: lane l
@@ -56,7 +57,11 @@ constexpr int kWaves = 4;
 constexpr int kQW = 32;              // query rows per wave
 constexpr int kBr = kWaves * kQW;    // query rows per workgroup
 constexpr int kWavesPP = 8;          // ping-pong kernel: waves per workgroup
-constexpr int kBrPP = kWavesPP * kQW;  // ping-pong kernel: query rows per workgroup
+constexpr int kBrPP = kWavesPP * kQW;  // ping-pong kernel: query rows per workgroup and block
+// 32-query blocks per wave of the ping-pong kernel: two at D = 64 without the mask (each K
+// or V fragment read from LDS then feeds two MFMAs, which halves the reads per MFMA that
+// bound the D = 64 matrix phase), else one.
+constexpr int pp_query_blocks(int D, bool causal) { return (D == 64 && !causal) ? 2 : 1; }
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold, in log2 units of probability
 
 struct Params {
@@ -421,7 +426,9 @@ void attn_fwd_kernel(const Params p) {
 }
 
 // ---- ping-pong kernel (D = 128, and non-causal D = 64 on grids that fill the device): one
-// workgroup of 8 waves (two per SIMD, one workgroup per compute unit) covers 256 queries.
+// workgroup of 8 waves (two per SIMD, one workgroup per compute unit) covers 256 queries,
+// or 512 at non-causal D = 64, where each wave takes two 32-query blocks (QB = 2) so that
+// every K and V fragment it reads from LDS feeds two MFMAs.
 // The waves form two groups (waves 0-3 are group 1, waves 4-7 group 0; waves w and w + 4
 // share a SIMD) that run the same sequence of phases offset by one:
 // a matrix phase (P V of tile j - 1, then the scores of tile j: MFMAs and the LDS reads
@@ -436,25 +443,29 @@ void attn_fwd_kernel(const Params p) {
 // MFMA, one K read per score MFMA) run kAhead MFMAs ahead of the MFMA that consumes them.
 // reads_through(m) counts the reads that MFMAs 0..m need. Three ahead measured 0.1-1%
 // faster than two, four no better.
-constexpr int reads_through(int m, int kPv) { return m < kPv ? 2 * (m + 1) : 2 * kPv + (m - kPv + 1); }
+constexpr int reads_through(int m, int kPv, int qb = 1) {
+  return m < kPv ? 2 * (m / qb + 1) : 2 * (kPv / qb) + ((m - kPv) / qb + 1);
+}
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
-template <int kPv, int M, int kAhead, int m>
+template <int kPv, int M, int kAhead, int QB, int m>
 __device__ inline void matrix_phase_step() {
   if constexpr (m < M) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA m
-    constexpr int n = reads_through(cmin(m + kAhead, M - 1), kPv) - reads_through(cmin(m + kAhead - 1, M - 1), kPv);
+    constexpr int n = reads_through(cmin(m + kAhead, M - 1), kPv, QB) -
+                      reads_through(cmin(m + kAhead - 1, M - 1), kPv, QB);
     if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);  // reads of MFMA m + kAhead
-    matrix_phase_step<kPv, M, kAhead, m + 1>();
+    matrix_phase_step<kPv, M, kAhead, QB, m + 1>();
   }
 }
-template <int D, int BC>
+// QB query blocks per wave: every LDS read feeds QB consecutive MFMAs.
+template <int D, int BC, int QB>
 __device__ inline void matrix_phase_schedule() {
-  constexpr int kPvMfma = (BC / 16) * (D / 32);
-  constexpr int kQkMfma = (BC / 32) * (D / 16);
+  constexpr int kPvMfma = QB * (BC / 16) * (D / 32);
+  constexpr int kQkMfma = QB * (BC / 32) * (D / 16);
   constexpr int M = kPvMfma + kQkMfma;
   constexpr int kAhead = 3;
-  __builtin_amdgcn_sched_group_barrier(0x100, reads_through(cmin(kAhead - 1, M - 1), kPvMfma), 0);
-  matrix_phase_step<kPvMfma, M, kAhead, 0>();
+  __builtin_amdgcn_sched_group_barrier(0x100, reads_through(cmin(kAhead - 1, M - 1), kPvMfma, QB), 0);
+  matrix_phase_step<kPvMfma, M, kAhead, QB, 0>();
 }
 
 template <int D, int BC, bool CAUSAL>
@@ -465,9 +476,11 @@ void attn_fwd_pp_kernel(const Params p) {
   constexpr int W = kWavesPP;
   constexpr int kBc = BC;
   constexpr int NB = BC / 32;
+  constexpr int QB = pp_query_blocks(D, CAUSAL);  // 32-query blocks per wave
+  constexpr int kQWave = QB * kQW;                 // query rows per wave
   using L = TileLayout<D, BC, W>;
   constexpr int RB = L::kRowBytes;
-  constexpr int kBrW = kBrPP;
+  constexpr int kBrW = W * kQWave;
   __shared__ __attribute__((aligned(1024))) char smem[L::kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -490,12 +503,12 @@ void attn_fwd_pp_kernel(const Params p) {
   const float c = p.c;
   const size_t head = (size_t)bh * (size_t)N * D;
   const __bf16* Qh = p.q + head;
-  const int q0 = qt * kBrW + wave * kQW;
-  const int qrow = q0 + col;
+  const int q0 = qt * kBrW + wave * kQWave;
+  const int qrow = q0 + col;  // this lane's row of query block 0 (block b: qrow + 32b)
   const bool wave_active = q0 < N;
   const int wg_kv_end = CAUSAL ? min(N, (qt + 1) * kBrW) : N;
   const int ntiles = (wg_kv_end + kBc - 1) / kBc;
-  const int T = !wave_active ? 0 : CAUSAL ? (min(N, q0 + kQW) + kBc - 1) / kBc : ntiles;
+  const int T = !wave_active ? 0 : CAUSAL ? (min(N, q0 + kQWave) + kBc - 1) / kBc : ntiles;
 
   // K/V copies (the layout and ragged-tile rule of attn_fwd_kernel). Only the four waves
   // of group 1 copy, and in the steady state they spread their copies through their
@@ -546,14 +559,17 @@ void attn_fwd_pp_kernel(const Params p) {
   auto copy_v = [&](int t, int i0, int i1) { copy_range(vrsrc, voff, LC::kPeriodV, t, vbuf_lds[t & 1], i0, i1); };
   if (grp == 1) copy_k(0, 0, LC::kCopies);
 
-  bf16x8 qf[D / 16];
-  if (qrow < N) {
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D) + hi;
+  bf16x8 qf[QB][D / 16];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = src[2 * s];
-  } else {
+  for (int b = 0; b < QB; ++b) {
+    if (qrow + kQW * b < N) {
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(Qh + (size_t)(qrow + kQW * b) * D) + hi;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = bf16x8{};
+      for (int s = 0; s < D / 16; ++s) qf[b][s] = src[2 * s];
+    } else {
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) qf[b][s] = bf16x8{};
+    }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
@@ -570,30 +586,40 @@ void attn_fwd_pp_kernel(const Params p) {
     v_addr[d] = row * RB + 16 * (chunk ^ swz_v<D>(row)) + 8 * (jj & 1);
   }
 
-  float m = -INFINITY;
-  float l = 0.f;
-  f32x16 o[D / 32];
+  // per query block b: running max m, sum l, O^T accumulators, scores and P
+  float m[QB], l[QB];
+  f32x16 o[QB][D / 32];
+  f32x16 s[QB][NB];
+  bf16x8 pb[QB][2 * NB];
 #pragma unroll
-  for (int d = 0; d < D / 32; ++d) o[d] = f32x16{};
-  f32x16 s[NB];
-  bf16x8 pb[2 * NB];
+  for (int b = 0; b < QB; ++b) {
+    m[b] = -INFINITY;
+    l[b] = 0.f;
 #pragma unroll
-  for (int j = 0; j < NB; ++j) s[j] = f32x16{};
+    for (int d = 0; d < D / 32; ++d) o[b][d] = f32x16{};
 #pragma unroll
-  for (int j = 0; j < 2 * NB; ++j) pb[j] = bf16x8{};
+    for (int j = 0; j < NB; ++j) s[b][j] = f32x16{};
+#pragma unroll
+    for (int j = 0; j < 2 * NB; ++j) pb[b][j] = bf16x8{};
+  }
 
   auto qk = [&](int t) {
     const int kb = (t & 1) * L::kTileBytes;
-    // the NB accumulation chains alternate, so consecutive MFMAs are independent
+    // the NB x QB accumulation chains alternate, so consecutive MFMAs are independent;
+    // each K fragment read serves the QB query blocks
 #pragma unroll
-    for (int j = 0; j < NB; ++j) s[j] = f32x16{};
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) s[b][j] = f32x16{};
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const char* a = smem + kb + k_addr[st] + 32 * j * RB;
-        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a), qf[st],
-                                                       s[j], 0, 0, 0);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(a);
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+          s[b][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[b][st], s[b][j], 0, 0, 0);
       }
     }
   };
@@ -607,7 +633,9 @@ void attn_fwd_pp_kernel(const Params p) {
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a0);
         const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
         const bf16x8 a = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st], o[d], 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+          o[b][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[b][st], o[b][d], 0, 0, 0);
       }
     }
   };
@@ -631,49 +659,53 @@ void attn_fwd_pp_kernel(const Params p) {
   // slot pair go out one at a time, evenly spaced between the exponentials (the
   // scheduling barriers keep them spread: 4 exponentials apart at D = 128).
   auto softmax = [&](int t, bool last, int copy_pair) {
-    if (last) {
-      const int key0 = t * kBc;
-      if ((key0 + kBc > N) || (CAUSAL && key0 + kBc - 1 > q0)) {
-        const int limit = (CAUSAL ? min(N, qrow + 1) : N) - key0 - 4 * hi;
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
+    for (int b = 0; b < QB; ++b) {
+      if (last) {
+        const int key0 = t * kBc;
+        if ((key0 + kBc > N) || (CAUSAL && key0 + kBc - 1 > q0 + kQW * b)) {
+          const int limit = (CAUSAL ? min(N, qrow + kQW * b + 1) : N) - key0 - 4 * hi;
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * j + 8 * (r >> 2) + (r & 3) >= limit) s[j][r] = -INFINITY;
-      }
-    }
-    float mx = m;
+          for (int j = 0; j < NB; ++j)
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
-    mx = max_across_halves(mx);
-    if (__builtin_amdgcn_ballot_w64((mx - m) * c > kRescaleLog2)) {
-      const float alpha = __builtin_amdgcn_exp2f((m - mx) * c);
-      m = mx;
-      l *= alpha;
-#pragma unroll
-      for (int d = 0; d < D / 32; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-    }
-    const float mc = m * c;
-    float rs = 0.f;
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        constexpr int kEvery = 16 * NB / kParts;
-        if (copy_pair >= 0 && (16 * j + r) % kEvery == 0) {
-          __builtin_amdgcn_sched_barrier(0);
-          copy_part(copy_pair, (16 * j + r) / kEvery);
-          __builtin_amdgcn_sched_barrier(0);
+            for (int r = 0; r < 16; ++r)
+              if (32 * j + 8 * (r >> 2) + (r & 3) >= limit) s[b][j][r] = -INFINITY;
         }
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][r], c, -mc));
-        rs += e;
-        pb[2 * j + (r >> 3)][r & 7] = (__bf16)e;
       }
-    l += rs;
+      float mx = m[b];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][j][r]);
+      mx = max_across_halves(mx);
+      if (__builtin_amdgcn_ballot_w64((mx - m[b]) * c > kRescaleLog2)) {
+        const float alpha = __builtin_amdgcn_exp2f((m[b] - mx) * c);
+        m[b] = mx;
+        l[b] *= alpha;
+#pragma unroll
+        for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[b][d][r] *= alpha;
+      }
+      const float mc = m[b] * c;
+      float rs = 0.f;
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          constexpr int kEvery = 16 * NB * QB / kParts;
+          const int e_idx = 16 * NB * b + 16 * j + r;  // exponential index in the tile
+          if (copy_pair >= 0 && e_idx % kEvery == 0) {
+            __builtin_amdgcn_sched_barrier(0);
+            copy_part(copy_pair, e_idx / kEvery);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][j][r], c, -mc));
+          rs += e;
+          pb[b][2 * j + (r >> 3)][r & 7] = (__bf16)e;
+        }
+      l[b] += rs;
+    }
   };
 
   // Slot pairs i = 0 .. ntiles (two barriers each). The copies of K(i+1) and V(i) are
@@ -695,7 +727,7 @@ void attn_fwd_pp_kernel(const Params p) {
     __builtin_amdgcn_s_setprio(2);
     pv(i - 1);
     qk(i);
-    matrix_phase_schedule<D, BC>();
+    matrix_phase_schedule<D, BC, QB>();
     __builtin_amdgcn_s_setprio(0);
   };
   wait_copies_and_barrier();
@@ -767,31 +799,36 @@ void attn_fwd_pp_kernel(const Params p) {
   }
 
   if (wave_active) {
-    const float lt = sum_across_halves(l);
-    if (qrow < N) {
-      const float inv = 1.f / lt;
-      __bf16* orow = p.o + head + (size_t)qrow * D;
 #pragma unroll
-      for (int d = 0; d < D / 32; ++d)
+    for (int b = 0; b < QB; ++b) {
+      const float lt = sum_across_halves(l[b]);
+      const int row = qrow + kQW * b;
+      if (row < N) {
+        const float inv = 1.f / lt;
+        __bf16* orow = p.o + head + (size_t)row * D;
 #pragma unroll
-        for (int j4 = 0; j4 < 4; ++j4) {
-          bf16x4 w;
+        for (int d = 0; d < D / 32; ++d)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = (__bf16)(o[d][4 * j4 + i] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * j4 + 4 * hi) = w;
-        }
-      if (hi == 0) p.lse[(size_t)bh * N + qrow] = (m * c + __builtin_log2f(lt)) * kLn2;
+          for (int j4 = 0; j4 < 4; ++j4) {
+            bf16x4 w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = (__bf16)(o[b][d][4 * j4 + i] * inv);
+            *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * j4 + 4 * hi) = w;
+          }
+        if (hi == 0) p.lse[(size_t)bh * N + row] = (m[b] * c + __builtin_log2f(lt)) * kLn2;
+      }
     }
   }
 }
 
 // Kernel choice. D = 128 runs the ping-pong kernel. D = 64 runs the ping-pong kernel when
-// the mask is off and its grid (one workgroup of 256 queries per compute unit) fills the
+// the mask is off and its grid (one workgroup of 512 queries per compute unit) fills the
 // device, else the four-wave kernel. At D = 64 a vector phase costs as much as at D = 128
 // while a matrix phase halves; measured on MI355X (interleaved, 200 launches each), the
-// ping-pong kernel is still 3-7% faster non-causal (B16 H16 N1024 to B1 H32 N4096), but
-// 10% slower causal, where the waves of a workgroup stop at different diagonal tiles, and
-// slower on grids that leave compute units idle (B1 H4 N8192: 570 vs 630 TFLOP/s).
+// ping-pong kernel with one query block per wave was already 3-7% faster non-causal
+// (B16 H16 N1024 to B1 H32 N4096), and two blocks per wave add 7-10%; it is 10% slower
+// causal, where the waves of a workgroup stop at different diagonal tiles, and slower on
+// grids that leave compute units idle (B1 H4 N8192: 570 vs 630 TFLOP/s).
 // attn_fwd_ex can force either kernel, for tests and tuning.
 bool use_pingpong(int D, int64_t pp_grid, int causal, int cus) {
   if (D == 128) return true;
@@ -861,7 +898,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   p.c = scale * kLog2e;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t n_qtiles_pp = ((int64_t)N + kBrPP - 1) / kBrPP;
+  const int64_t rows_pp = (int64_t)kBrPP * pp_query_blocks(D, causal != 0);
+  const int64_t n_qtiles_pp = ((int64_t)N + rows_pp - 1) / rows_pp;
   const int64_t grid_pp = (int64_t)B * H * n_qtiles_pp;
   bool pingpong = kernel == ATTN_FWD_KERNEL_PINGPONG;
   if (kernel == ATTN_FWD_KERNEL_AUTO) {

@@ -126,6 +126,9 @@ LARGE_GRID_SHAPES = [
     # B, H, N, D
     (16, 20, 256, 128), (64, 16, 512, 128), (16, 16, 1024, 64), (5, 9, 2500, 64),
     (11, 7, 1000, 128), (4, 5, 4097, 128), (2, 130, 300, 128),
+    # D = 64 ping-pong waves hold two 32-query blocks: a last wave whose second block is
+    # partly past N (545 = 512 + 33) and one whose second block is wholly past it (1600)
+    (3, 5, 545, 64), (7, 3, 1600, 64),
 ]
 
 
