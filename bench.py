@@ -22,7 +22,8 @@ Reported:
   roofline       F over the mean duration of one call (HIP events on the launch stream)
                  against the bf16 dense MFMA peak
   cpu_baseline   the fp64 numpy oracle of the same pass, timed on this host's cores on a
-                 bounded sample of the same workload (a few heads), in the same unit
+                 bounded sample of the same workload (a few heads), in the same unit, with
+                 the threads it used ("cores") and the host CPU's model name ("cpu")
 """
 from __future__ import annotations
 
@@ -73,6 +74,43 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("unknown" where it cannot be read)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def mfma_sustained(stream, iterations: int = 25000, reps: int = 4):
+    """Rates of the sustained matrix-core probe (include/tile_calibrate.h): the best of
+    ``reps`` runs with zero operands and with random bf16 operands, each ~25 ms."""
+    import torch
+
+    from softmax_attention_fwd_amd import mfma_calibrate
+    rates = {}
+    for random_operands in (False, True):
+        best = 0.0
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            flops = mfma_calibrate(iterations, random_operands, stream=stream)
+            e1.record(stream)
+            e1.synchronize()
+            best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        key = "random_tflops" if random_operands else "zeros_tflops"
+        rates[key] = round(best, 1)
+        log(f"[bench] sustained MFMA probe, {'random' if random_operands else 'zero'} operands: "
+            f"{best:.1f} TFLOP/s ({100 * best / PEAK_BF16_TFLOPS:.1f}% of {PEAK_BF16_TFLOPS})")
+    rates["peak_frac_random"] = round(rates["random_tflops"] / PEAK_BF16_TFLOPS, 4)
+    return rates
+
+
 def cpu_baseline(w, q, k, v, budget_s: float, do=None):
     """Time the fp64 oracle (forward, or backward when ``do`` is given) on whole heads of
     the workload, one head per host core."""
@@ -114,7 +152,7 @@ def cpu_baseline(w, q, k, v, budget_s: float, do=None):
     return {
         "value": round(done * per_head / dt / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": cores,
+        "cores": cores, "cpu": cpu_model(),
         "kind": "oracle",
         "sample": (f"{done} head-passes ({'forward' if do is None else 'backward'}) of "
                    f"{w.describe()} (first {heads} heads, "
@@ -185,7 +223,7 @@ def decode_cpu_baseline(w, q, k, v, budget_s: float):
     return {
         "value": round(done * per_head / dt / 1e9, 4),
         "unit": "GB/s",
-        "cores": cores,
+        "cores": cores, "cpu": cpu_model(),
         "kind": "oracle",
         "sample": (f"{done} head-passes (decode) of {w.describe()} (first {heads} heads, "
                    f"{done * per_head / 1e9:.3f} GB of K/V/Q/O, fp64 numpy, one head per thread) "
@@ -314,7 +352,7 @@ def run_gemm(args) -> int:
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {
             "value": round(done * 2.0 * rows * N * K / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": cores, "kind": "oracle",
+            "cores": cores, "cpu": cpu_model(), "kind": "oracle",
             "sample": f"{done} products of the first {rows} rows of A with B (fp64 numpy, BLAS threads "
                       f"as numpy sets them) in {dt:.1f} s"}
         log(f"[bench] cpu baseline: {result['cpu_baseline']}")
@@ -387,7 +425,7 @@ def run_based(args) -> int:
                 break
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {
-            "value": round(done * per_head / dt / 1e9, 6), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "value": round(done * per_head / dt / 1e9, 6), "unit": "GB/s", "cores": cores, "cpu": cpu_model(), "kind": "oracle",
             "sample": f"{done} heads of {w.describe()} by the quadratic definition (fp64 numpy, BLAS "
                       f"threads as numpy sets them) in {dt:.1f} s"}
         log(f"[bench] cpu baseline: {result['cpu_baseline']}")
@@ -414,6 +452,10 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device-to-device copy (3 times) so that "
                          "hardware byte counters can be scaled against a kernel of known traffic")
+    ap.add_argument("--calibrate-mfma", action="store_true",
+                    help="after the timed steps, run the sustained matrix-core probe (4 x ~25 ms "
+                         "with zero operands, then 4 with random bf16 operands) and report its "
+                         "rates under \"mfma_sustained\"")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -519,6 +561,8 @@ def main() -> int:
         torch.cuda.synchronize()
         log("[bench] calibration copy: 3 x 512 MiB device-to-device")
         del src, dst
+    if args.calibrate_mfma:
+        result["mfma_sustained"] = mfma_sustained(stream)
     if not args.no_cpu_baseline:
         log(f"[bench] timing the fp64 oracle on host cores (~{args.cpu_seconds:.0f} s budget)")
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds, do=do)

@@ -6,7 +6,8 @@ device pointers and the current HIP stream. Every step of the computation runs i
 library's HIP kernels; if the library is missing this module raises instead of computing
 anything itself.
 
-C entry points (declared in include/attn_fwd.h, attn_bwd.h, attn_decode.h, tile_gemm.h):
+C entry points (declared in include/attn_fwd.h, attn_bwd.h, attn_decode.h, tile_gemm.h,
+based_fwd.h, tile_calibrate.h):
   int attn_fwd(q, k, v, o, lse, B, H, N, D, causal, scale, stream)
   int attn_fwd_ex(q, k, v, o, lse, B, H, N, D, causal, scale, kernel, stream)
   const char* attn_fwd_strerror(int code)
@@ -21,6 +22,10 @@ C entry points (declared in include/attn_fwd.h, attn_bwd.h, attn_decode.h, tile_
   const char* attn_decode_strerror(int code)
   int gemm_bf16_nt(a, b, c, M, N, K, stream)
   const char* gemm_strerror(int code)
+  int based_fwd(q, k, v, o, B, H, N, D, F, stream)
+  const char* based_fwd_strerror(int code)
+  size_t tile_mfma_calibrate_out_floats(void)
+  int tile_mfma_calibrate(out, out_floats, iterations, random_operands, flops, stream)
 """
 from __future__ import annotations
 
@@ -102,6 +107,10 @@ def load_library():
         lib.based_fwd.restype = ci
         lib.based_fwd_strerror.argtypes = [ci]
         lib.based_fwd_strerror.restype = ctypes.c_char_p
+        lib.tile_mfma_calibrate_out_floats.argtypes = []
+        lib.tile_mfma_calibrate_out_floats.restype = sz
+        lib.tile_mfma_calibrate.argtypes = [vp, sz, ci, ci, ctypes.POINTER(ctypes.c_double), vp]
+        lib.tile_mfma_calibrate.restype = ci
         _lib = lib
         return lib
 
@@ -435,3 +444,26 @@ def based_fwd(q, k, v, out=None, stream=None):
             raise ValueError(f"based_fwd rejected its arguments (code {code}): {msg}")
         raise BasedFwdError(code, msg)
     return out
+
+
+def mfma_calibrate(iterations: int, random_operands: bool, out=None, stream=None) -> float:
+    """Enqueue the sustained matrix-core probe (include/tile_calibrate.h) on the current
+    CUDA device and return the floating-point operations it performs. ``out`` (float32,
+    at least tile_mfma_calibrate_out_floats() elements) is allocated when not given; time
+    the call with events on ``stream`` (default: torch's current stream)."""
+    import torch
+
+    lib = load_library()
+    need = int(lib.tile_mfma_calibrate_out_floats())
+    if need == 0:
+        raise RuntimeError("tile_mfma_calibrate_out_floats: device query failed")
+    dev = torch.device("cuda", torch.cuda.current_device())
+    if out is None:
+        out = torch.empty(need, dtype=torch.float32, device=dev)
+    flops = ctypes.c_double(0.0)
+    code = lib.tile_mfma_calibrate(out.data_ptr(), out.numel(), int(iterations),
+                                   int(bool(random_operands)), ctypes.byref(flops),
+                                   _stream_handle(stream, dev))
+    if code != 0:
+        raise RuntimeError(f"tile_mfma_calibrate failed with code {code}")
+    return flops.value

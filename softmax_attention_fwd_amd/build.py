@@ -2,11 +2,12 @@
 
     python -m softmax_attention_fwd_amd.build        # or __graft_entry__.build()
 
-The library holds five translation units, each with its kernels and C entry points:
+The library holds six translation units, each with its kernels and C entry points:
 csrc/attn_fwd.hip (the forward), csrc/attn_bwd.hip (the backward),
 csrc/attn_decode.hip (the decode-shaped split-KV forward), csrc/gemm.hip (the plain
-bf16 matrix product on the same tile layer) and csrc/based_fwd.hip (Based linear
-attention). It is built for
+bf16 matrix product on the same tile layer), csrc/based_fwd.hip (Based linear
+attention) and csrc/calibrate.hip (the sustained matrix-core rate probe that bench.py
+reads measured rates against). It is built for
 gfx950 only, with packed fp32 VALU instructions disabled (the compiler would otherwise
 form v_pk_* fp32 ops from plain float code).
 """
@@ -19,7 +20,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "gemm.hip", "based_fwd.hip")]
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "gemm.hip",
+                                                 "based_fwd.hip", "calibrate.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libattn_fwd.so")
 ARCH = "gfx950"

@@ -52,13 +52,17 @@ def test_header_declares_entry_points():
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "based_fwd.h")).read(), flags=re.S)
     assert sorted(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(based_\w+)\s*\(", text, flags=re.M)) == \
         ["based_fwd", "based_fwd_strerror"]
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "tile_calibrate.h")).read(), flags=re.S)
+    assert sorted(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(tile_\w+)\s*\(", text, flags=re.M)) == \
+        ["tile_mfma_calibrate", "tile_mfma_calibrate_out_floats"]
 
 
 def test_exports_every_declared_symbol(lib):
     import subprocess
     exported = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
                               capture_output=True, text=True, check=True).stdout.split()
-    for name in declared_functions() + ["gemm_bf16_nt", "gemm_strerror", "based_fwd", "based_fwd_strerror"]:
+    for name in declared_functions() + ["gemm_bf16_nt", "gemm_strerror", "based_fwd", "based_fwd_strerror",
+                                        "tile_mfma_calibrate", "tile_mfma_calibrate_out_floats"]:
         assert hasattr(lib, name), f"{name} declared in include/ but not exported"
         assert name in exported
 
@@ -311,3 +315,13 @@ def test_based_binding_rejects_cpu_and_bad_shapes():
         based_fwd(q.float(), q, v)
     with pytest.raises(TypeError):
         based_fwd(q.numpy(), q, v)
+
+
+def test_mfma_calibrate_rejects_bad_arguments(lib):
+    # argument checks that come before any device query
+    flops = ctypes.c_double(0.0)
+    assert lib.tile_mfma_calibrate(None, 1 << 20, 10, 1, ctypes.byref(flops), None) == -1
+    assert lib.tile_mfma_calibrate(A, 1 << 20, 0, 1, ctypes.byref(flops), None) == -1
+    assert lib.tile_mfma_calibrate(A, 1 << 20, 10, 2, ctypes.byref(flops), None) == -1
+    assert lib.tile_mfma_calibrate(A, 1 << 20, (1 << 24) + 1, 0, ctypes.byref(flops), None) == -1
+    assert lib.tile_mfma_calibrate(A, 1 << 20, 10, 0, None, None) == -1
