@@ -72,7 +72,8 @@ struct Params {
   float* lse;
   int N;
   int n_qtiles;  // ceil(N / kBr)
-  int remap;     // 1: grid size is a multiple of 8, use the XCD-aware order
+  int n_units;   // ping-pong kernel: B * H * n_qtiles work units (the grid may be smaller)
+  int remap;     // 1: grid size (ping-pong: unit count) is a multiple of 8, use the XCD order
   float c;       // scale * log2(e)
 };
 
@@ -495,7 +496,16 @@ void attn_fwd_pp_kernel(const Params p) {
   const int col = lane & 31;
   const int hi = lane >> 5;
 
-  const int g = remap_block(blockIdx.x, p.remap);
+  // Work units. Causal: one per workgroup (the loop below runs once), since the hardware
+  // dispatches the grid longest units first, which balances units of different lengths
+  // better than a fixed assignment. Non-causal: persistent when the launch has fewer
+  // workgroups than units (one per compute unit): workgroup b walks units b,
+  // b + gridDim.x, ...; the XCD order is taken over the units, so each XCD runs
+  // consecutive units of the same heads.
+  for (int gu = blockIdx.x;; gu += gridDim.x) {
+  if (!CAUSAL && gu >= p.n_units) break;
+  const int g = CAUSAL ? remap_block(blockIdx.x, p.remap)
+                       : (p.remap ? (gu & 7) * (p.n_units >> 3) + (gu >> 3) : gu);
   const int bh = g / p.n_qtiles;
   int qt = g - bh * p.n_qtiles;
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;
@@ -723,10 +733,55 @@ void attn_fwd_pp_kernel(const Params p) {
       if (i < ntiles) copy_v(i, 0, LC::kCopies);
     }
   };
+  // A full matrix phase: the P V MFMAs of tile i-1 (key step st, output block d, in that
+  // order), then the score MFMAs of tile i (step st, key block j), each LDS read feeding
+  // its QB MFMAs. In the non-causal kernel, whose persistent loop leaves the compiler
+  // fewer registers, it is written software-pipelined in the source: the A operand of
+  // read r+3 is read before the MFMAs of read r, into one of four rotating fragments.
+  // Where a scheduling region runs short of registers the compiler keeps the source order;
+  // written this way that order still hides the LDS latency (a fragment read right before
+  // its MFMA would make every MFMA wait for its read). Same MFMAs in the same order as
+  // pv + qk, so the same bits.
   auto matrix = [&](int i) {  // P V of tile i-1 and scores of tile i, both present
     __builtin_amdgcn_s_setprio(2);
-    pv(i - 1);
-    qk(i);
+    if constexpr (CAUSAL) {
+      pv(i - 1);
+      qk(i);
+    } else {
+      constexpr int kPvR = (kBc / 16) * (D / 32);
+      constexpr int kR = kPvR + (D / 16) * NB;
+      const int vb = 2 * L::kTileBytes + ((i - 1) & 1) * L::kTileBytes;
+      const int kb = (i & 1) * L::kTileBytes;
+      auto operand = [&](int r) {
+        if (r < kPvR) {  // V^T fragment of key step r / (D/32), output block r % (D/32)
+          const char* a0 = smem + vb + v_addr[r % (D / 32)] + 16 * (r / (D / 32)) * RB;
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a0);
+          const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 8 * RB));
+          return __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        const int q = r - kPvR;  // K fragment of step q / NB, key block q % NB
+        return *reinterpret_cast<const bf16x8*>(smem + kb + k_addr[q / NB] + 32 * (q % NB) * RB);
+      };
+      bf16x8 fr[4];
+      fr[0] = operand(0);
+      fr[1] = operand(1);
+      fr[2] = operand(2);
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        if (r + 3 < kR) fr[(r + 3) & 3] = operand(r + 3);
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+          if (r < kPvR) {
+            const int d = r % (D / 32);
+            o[b][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[r & 3], pb[b][r / (D / 32)], o[b][d], 0, 0, 0);
+          } else {
+            const int q = r - kPvR, j = q % NB;
+            s[b][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[r & 3], qf[b][q / NB],
+                                                             q < NB ? f32x16{} : s[b][j], 0, 0, 0);
+          }
+        }
+      }
+    }
     matrix_phase_schedule<D, BC, QB>();
     __builtin_amdgcn_s_setprio(0);
   };
@@ -819,6 +874,8 @@ void attn_fwd_pp_kernel(const Params p) {
       }
     }
   }
+  if (CAUSAL) break;
+  }  // work units
 }
 
 // Kernel choice. D = 128 runs the ping-pong kernel. D = 64 runs the ping-pong kernel when
@@ -912,8 +969,18 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   }
   if (pingpong) {
     p.n_qtiles = (int)n_qtiles_pp;
+    p.n_units = (int)grid_pp;
     p.remap = (grid_pp % 8 == 0) ? 1 : 0;
-    const dim3 gpp((unsigned)grid_pp), bpp(64 * kWavesPP);
+    // non-causal launches with more units than compute units: a persistent grid of one
+    // workgroup per compute unit (a multiple of 8: the same share of every XCD)
+    int cus = 0;
+    if (!causal) {
+      const int rc = device_cus(&cus);
+      if (rc != ATTN_FWD_OK) return rc;
+    }
+    const int64_t persistent = (!causal && cus >= 8) ? cus / 8 * 8 : 0;
+    const dim3 gpp((unsigned)(persistent > 0 && grid_pp > persistent ? persistent : grid_pp)),
+        bpp(64 * kWavesPP);
     if (D == 64) {
       if (causal) hipLaunchKernelGGL((attn_fwd_pp_kernel<64, 64, true>), gpp, bpp, 0, s, p);
       else hipLaunchKernelGGL((attn_fwd_pp_kernel<64, 64, false>), gpp, bpp, 0, s, p);
