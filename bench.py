@@ -378,9 +378,14 @@ def run_based(args) -> int:
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     o = torch.empty_like(vd)
     stream = torch.cuda.current_stream(dev)
+    from softmax_attention_fwd_amd.binding import based_fwd_workspace_bytes
+    need = based_fwd_workspace_bytes(w.B, w.H, w.N)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
+    if need > 0:
+        log(f"[bench] split launch: {need / 2**20:.1f} MiB of segment states")
 
     def step():
-        based_fwd(qd, kd, vd, out=o, stream=stream)
+        based_fwd(qd, kd, vd, out=o, workspace=ws, stream=stream)
 
     total_ms, launch_ms, wall = time_steps(step, stream, args.steps, args.warmup)
     mean_launch = statistics.fmean(launch_ms)

@@ -29,9 +29,10 @@ extern "C" {
 /* Return codes. */
 #define BASED_OK            0   /* success: the kernel was enqueued on the stream          */
 #define BASED_EINVAL       -1   /* NULL pointer; B, H or N < 1; N*dv*2 >= 2^31 bytes per
-                                   head, or B*H >= 2^31 workgroups                          */
+                                   head, or B*H >= 2^24                                      */
 #define BASED_EUNSUPPORTED -2   /* d other than 16 or dv other than 64                      */
-#define BASED_EALIGN       -3   /* q, k, v or o not 16-byte aligned                         */
+#define BASED_EALIGN       -3   /* q, k, v or o not 16-byte aligned, or the workspace not
+                                   256-byte aligned                                          */
 #define BASED_ELAUNCH      -4   /* hipGetLastError() was set after the launch (this also
                                    reports, and clears, an error left pending by an earlier
                                    HIP call on the calling thread)                           */
@@ -58,6 +59,30 @@ extern "C" {
  */
 int based_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
               int dv, void* stream);
+
+/*
+ * based_fwd_workspace_bytes - device workspace that based_fwd_ws needs to split each head's
+ * sequence over several workgroups on the current device: fp32 running states of every
+ * segment but the last, 163840 bytes per (batch, head, segment). 0 when no split pays
+ * (B*H at least the device's compute-unit count, or sequences under 16 chunks of 64
+ * tokens) or the device query fails.
+ */
+size_t based_fwd_workspace_bytes(int B, int H, int N);
+
+/*
+ * based_fwd_ws - based_fwd with an optional caller-owned workspace (256-byte aligned; its
+ * contents on entry do not matter). With workspace_bytes >= based_fwd_workspace_bytes(B,
+ * H, N) > 0, each head's chunks are cut into segments of at least 8 chunks, enough for
+ * B*H*segments workgroups to cover the device's compute units: a first kernel sums each
+ * segment's contribution to the running state, and the second runs one workgroup per
+ * (batch, head, segment), each starting from the sum of the segments before it. Otherwise
+ * (NULL or a smaller workspace) it runs as based_fwd. Same arguments, ownership and
+ * behaviour as based_fwd otherwise; the split changes only the order of the fp32 sums
+ * of the running state (results agree with based_fwd to rounding, not bit for bit).
+ * Concurrent calls must use different workspaces.
+ */
+int based_fwd_ws(const void* q, const void* k, const void* v, void* o, void* workspace,
+                 size_t workspace_bytes, int B, int H, int N, int d, int dv, void* stream);
 
 /* based_fwd_strerror - a static, NUL-terminated description of a return code. */
 const char* based_fwd_strerror(int code);

@@ -23,6 +23,8 @@ based_fwd.h, tile_calibrate.h):
   int gemm_bf16_nt(a, b, c, M, N, K, stream)
   const char* gemm_strerror(int code)
   int based_fwd(q, k, v, o, B, H, N, D, F, stream)
+  size_t based_fwd_workspace_bytes(B, H, N)
+  int based_fwd_ws(q, k, v, o, workspace, workspace_bytes, B, H, N, D, F, stream)
   const char* based_fwd_strerror(int code)
   size_t tile_mfma_calibrate_out_floats(void)
   int tile_mfma_calibrate(out, out_floats, iterations, random_operands, flops, stream)
@@ -105,6 +107,10 @@ def load_library():
         lib.gemm_strerror.restype = ctypes.c_char_p
         lib.based_fwd.argtypes = [vp] * 4 + [ci] * 5 + [vp]
         lib.based_fwd.restype = ci
+        lib.based_fwd_workspace_bytes.argtypes = [ci, ci, ci]
+        lib.based_fwd_workspace_bytes.restype = sz
+        lib.based_fwd_ws.argtypes = [vp] * 5 + [sz] + [ci] * 5 + [vp]
+        lib.based_fwd_ws.restype = ci
         lib.based_fwd_strerror.argtypes = [ci]
         lib.based_fwd_strerror.restype = ctypes.c_char_p
         lib.tile_mfma_calibrate_out_floats.argtypes = []
@@ -415,10 +421,19 @@ class BasedFwdError(RuntimeError):
         self.code = code
 
 
-def based_fwd(q, k, v, out=None, stream=None):
+def based_fwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    """Workspace for based_fwd to split each head's sequence on the current device (0: no
+    split pays)."""
+    return int(load_library().based_fwd_workspace_bytes(int(B), int(H), int(N)))
+
+
+def based_fwd(q, k, v, out=None, workspace=None, split=True, stream=None):
     """Based linear attention (causal) on the GPU: q, k [B, H, N, 16] and v [B, H, N, 64],
     contiguous bfloat16 CUDA tensors on one device. Returns o bfloat16 [B, H, N, 64]
-    (``out`` to write in place)."""
+    (``out`` to write in place). When B*H leaves compute units idle and ``split`` is true,
+    each head's sequence is split over several workgroups (based_fwd_ws); ``workspace`` (a
+    uint8 CUDA tensor of at least based_fwd_workspace_bytes(B, H, N) bytes) is allocated
+    when not given."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -436,8 +451,19 @@ def based_fwd(q, k, v, out=None, stream=None):
           or out.device != q.device):
         raise ValueError("out must be a contiguous bfloat16 [B, H, N, 64] tensor on q's device")
     lib = load_library()
-    code = lib.based_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d, dv,
-                         _stream_handle(stream, q.device))
+    need = int(lib.based_fwd_workspace_bytes(B, H, N)) if split else 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        elif (workspace.dtype != torch.uint8 or workspace.device != q.device
+              or not workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+        code = lib.based_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                workspace.data_ptr(), workspace.numel(), B, H, N, d, dv,
+                                _stream_handle(stream, q.device))
+    else:
+        code = lib.based_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, d, dv,
+                             _stream_handle(stream, q.device))
     if code != ATTN_FWD_OK:
         msg = lib.based_fwd_strerror(code).decode()
         if code in (ATTN_FWD_EINVAL, ATTN_FWD_EUNSUPPORTED, ATTN_FWD_EALIGN):

@@ -36,6 +36,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "based_fwd.h"
 #include "tile_lds.h"
 
@@ -68,9 +70,22 @@ struct BasedParams {
   const __bf16* k;
   const __bf16* v;
   __bf16* o;
+  float* ws;       // segment states (split launches), else unused
   int N;
   int n_chunks;
+  int n_seg;       // segments per head (1: one workgroup per head)
+  int seg_chunks;  // chunks per segment (the last segment may be shorter)
 };
+
+// Split launches: a head's chunks are cut into n_seg segments of seg_chunks. A state pass
+// (based_state_kernel) writes, for every segment but the last, the fp32 sums of its
+// chunks in two halves (group 0 took the even chunks, group 1 the odd ones) in the
+// register layout of the state waves: for state wave u and lane l, slot j in [0, 80) at
+// ((u * kWsSlots + j) * 64 + l): 0-63 the quadratic tiles, 64-67 the linear, 68-71 the
+// constant features, 72-75 KK and 76 the lane's share of ksum (wave 0). The output pass
+// starts each segment's state waves from the sum of the earlier segments' halves.
+constexpr int kWsSlots = 80;
+constexpr int kWsGroup = 4 * kWsSlots * 64;  // floats of one half-segment state
 
 // V chunk tiles (128-byte rows) keep their 16-byte chunks permuted: logical chunk j of row r
 // at j ^ swz_v(r). A transposing read covers, per 32 lanes, 8 consecutive rows and two
@@ -136,9 +151,8 @@ struct HeadRefs {
   uint32_t smem_lds;
 };
 
-__device__ inline HeadRefs head_refs(const BasedParams& p, char* smem) {
+__device__ inline HeadRefs head_refs(const BasedParams& p, char* smem, size_t bh) {
   const int N = p.N;
-  const size_t bh = blockIdx.x;
   HeadRefs h;
   h.qr = make_rsrc(p.q + bh * N * kD, (uint32_t)N * kD * 2);
   h.kr = make_rsrc(p.k + bh * N * kD, (uint32_t)N * kD * 2);
@@ -161,16 +175,17 @@ __device__ inline bf16x8 v_frag(const char* Vs, int m, int cb, int g, int c) {
 // S^T, KK and ksum published after the previous chunk; computes O_inter, O_intra, the
 // normaliser and stores o.
 template <int W>
-__device__ inline void output_wave(const BasedParams& p, char* smem, int lane) {
+__device__ inline void output_wave(const BasedParams& p, char* smem, int lane, size_t bh, int t_begin,
+                                   int t_end) {
   const int g = lane >> 4;  // 16-lane row
   const int c = lane & 15;  // lane within the row
   const int N = p.N;
-  const HeadRefs hr = head_refs(p, smem);
-  copy_one(hr.qr, hr.kr, hr.vr, W, 0, N, hr.smem_lds, lane);
+  const HeadRefs hr = head_refs(p, smem, bh);
+  copy_one(hr.qr, hr.kr, hr.vr, W, t_begin * kChunk, N, hr.smem_lds, lane);
   wait_copies_and_barrier();
-  for (int t = 0; t < p.n_chunks; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < p.n_chunks) copy_one(hr.qr, hr.kr, hr.vr, W, (t + 1) * kChunk, N, hr.smem_lds + (cur ^ 1) * kStage, lane);
+  for (int t = t_begin; t < t_end; ++t) {
+    const int cur = (t - t_begin) & 1;
+    if (t + 1 < t_end) copy_one(hr.qr, hr.kr, hr.vr, W, (t + 1) * kChunk, N, hr.smem_lds + (cur ^ 1) * kStage, lane);
     const char* Qs = smem + cur * kStage;
     const char* Ks = Qs + kQBytes;
     const char* Vs = Ks + kQBytes;
@@ -288,137 +303,290 @@ __device__ inline void output_wave(const BasedParams& p, char* smem, int lane) {
   }
 }
 
-// State wave U (0..3): owns the quadratic features with a in [4U, 4U + 4) for all value
-// columns and the linear and constant features of value columns 16U .. 16U + 15 (wave 0
-// also KK and ksum). Adds each chunk's contribution and publishes the bf16 S^T (and KK,
-// ksum) in the other buffer for the next chunk's output waves.
-template <int U>
-__device__ inline void state_wave(const BasedParams& p, char* smem, int lane) {
-  const int g = lane >> 4;
-  const int c = lane & 15;
-  const int N = p.N;
-  const HeadRefs hr = head_refs(p, smem);
-  copy_one(hr.qr, hr.kr, hr.vr, 4 + 2 * U, 0, N, hr.smem_lds, lane);
-  copy_one(hr.qr, hr.kr, hr.vr, 5 + 2 * U, 0, N, hr.smem_lds, lane);
-
+// The running state of state wave U (0..3): the quadratic features with a in [4U, 4U + 4)
+// for all value columns, the linear and constant features of value columns 16U .. 16U + 15,
+// and (wave 0) KK and this lane's share of ksum.
+struct StateRegs {
   f32x4 sq[4][4];  // quadratic features (a = 4U + rb, b = 4g + i) x value columns 16cb + c
+  f32x4 slin;      // linear features b = 4g + i (value / 2) x value columns 16U + c
+  f32x4 sconst;    // row 0: sum of v over value columns 16U + c; rows 1-15 stay zero
+  f32x4 kk;        // wave 0: KK[a = 4g + i][b = c]
+  float ksum_part; // wave 0: sum of k[token][c] over this lane's tokens
+};
+
+__device__ inline void state_zero(StateRegs& st) {
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) sq[rb][cb] = f32x4{};
-  f32x4 slin = {};   // linear features b = 4g + i (value / 2) x value columns 16U + c
-  f32x4 sconst = {}; // row 0: sum of v over value columns 16U + c; rows 1-15 stay zero
-  f32x4 kk = {};     // wave 0: KK[a = 4g + i][b = c]
-  float ksum_part = 0.f;  // wave 0: sum of k[token][c] over this lane's tokens
+    for (int cb = 0; cb < 4; ++cb) st.sq[rb][cb] = f32x4{};
+  st.slin = f32x4{};
+  st.sconst = f32x4{};
+  st.kk = f32x4{};
+  st.ksum_part = 0.f;
+}
+
+// S += phi(K)^T V, KK += K^T K, ksum += sum k for the chunk whose K and V tiles are at Ks, Vs
+// (rows past N are zeros and add nothing).
+template <int U>
+__device__ inline void state_update(StateRegs& st, const char* Ks, const char* Vs, int g, int c) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const char* k0 = Ks + (32 * m + 4 * g + (c >> 2)) * 32 + 8 * (c & 3);
+    const bf16x8 kc = __builtin_shufflevector(tr4(k0), tr4(k0 + 16 * 32), 0, 1, 2, 3, 4, 5, 6, 7);
+    float kf[8], kfs[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      kf[j] = (float)kc[j];  // k[token_j][c]
+      kfs[j] = kf[j] * kC2;
+    }
+    bf16x8 vfm[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) vfm[cb] = v_frag(Vs, m, cb, g, c);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)  // k[token_j][4U + rb] from lane 4U + rb of this row
+        f[j] = __uint_as_float(row_bcast_feature<U>(__float_as_uint(kf[j]), rb)) * kfs[j];
+      const bf16x8 afeat = pack8(f);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+        st.sq[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afeat, vfm[cb], st.sq[rb][cb], 0, 0, 0);
+    }
+    float fl[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fl[j] = 0.5f * kf[j];
+    st.slin = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(fl), vfm[U], st.slin, 0, 0, 0);
+    bf16x8 ones;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ones[j] = (__bf16)(c == 0 ? 1.f : 0.f);
+    st.sconst = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, vfm[U], st.sconst, 0, 0, 0);
+    if (U == 0) {
+      st.kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, kc, st.kk, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st.ksum_part += kf[j];
+    }
+  }
+}
+
+// Publish the bf16 S^T (and, wave 0, KK as a hi + lo pair and ksum) into buffer `buf`.
+template <int U>
+__device__ inline void state_publish(const StateRegs& st, char* smem, int buf, int g, int c) {
+  char* Stn = smem + kOffSt + buf * kStBytes;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      bf16x4 x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = (__bf16)st.sq[rb][cb][i];
+      *reinterpret_cast<bf16x4*>(Stn + (16 * cb + c) * (kStRow * 2) + 2 * (16 * (4 * U + rb) + 4 * g)) = x;
+    }
+  {
+    bf16x4 xl, xc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xl[i] = (__bf16)st.slin[i];
+      xc[i] = (__bf16)st.sconst[i];
+    }
+    *reinterpret_cast<bf16x4*>(Stn + (16 * U + c) * (kStRow * 2) + 2 * (256 + 4 * g)) = xl;
+    *reinterpret_cast<bf16x4*>(Stn + (16 * U + c) * (kStRow * 2) + 2 * (272 + 4 * g)) = xc;
+  }
+  if (U == 0) {
+    __bf16* KKn = reinterpret_cast<__bf16*>(smem + kOffKK + buf * kKKBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 hi = (__bf16)st.kk[i];
+      KKn[(4 * g + i) * kD + c] = hi;
+      KKn[256 + (4 * g + i) * kD + c] = (__bf16)(st.kk[i] - (float)hi);
+    }
+    const float ks = sum_across_halves(sum_across_16(st.ksum_part));
+    if (g == 0) reinterpret_cast<float*>(smem + kOffKs)[buf * kD + c] = ks;
+  }
+}
+
+// Segment-state slots of state wave U: read (add) or write this lane's registers.
+template <int U>
+__device__ inline void state_add_from(StateRegs& st, const float* w, int lane) {
+  const float* b = w + (size_t)U * kWsSlots * 64 + lane;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.sq[rb][cb][i] += b[(16 * rb + 4 * cb + i) * 64];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    st.slin[i] += b[(64 + i) * 64];
+    st.sconst[i] += b[(68 + i) * 64];
+  }
+  if (U == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.kk[i] += b[(72 + i) * 64];
+    st.ksum_part += b[76 * 64];
+  }
+}
+template <int U>
+__device__ inline void state_store_to(const StateRegs& st, float* w, int lane) {
+  float* b = w + (size_t)U * kWsSlots * 64 + lane;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[(16 * rb + 4 * cb + i) * 64] = st.sq[rb][cb][i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b[(64 + i) * 64] = st.slin[i];
+    b[(68 + i) * 64] = st.sconst[i];
+    b[(72 + i) * 64] = U == 0 ? st.kk[i] : 0.f;
+  }
+  b[76 * 64] = U == 0 ? st.ksum_part : 0.f;
+}
+
+// State wave U (0..3) of the output pass: starts from the state of the segments before
+// `seg` (zero for the first) and adds each chunk's contribution, publishing the bf16 S^T
+// (and KK, ksum) in the other buffer for the next chunk's output waves.
+template <int U>
+__device__ inline void state_wave(const BasedParams& p, char* smem, int lane, size_t bh, int seg,
+                                  int t_begin, int t_end) {
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const int N = p.N;
+  const HeadRefs hr = head_refs(p, smem, bh);
+  copy_one(hr.qr, hr.kr, hr.vr, 4 + 2 * U, t_begin * kChunk, N, hr.smem_lds, lane);
+  copy_one(hr.qr, hr.kr, hr.vr, 5 + 2 * U, t_begin * kChunk, N, hr.smem_lds, lane);
+
+  StateRegs st;
+  state_zero(st);
+  if (seg > 0) {
+    const float* w = p.ws + bh * (size_t)(p.n_seg - 1) * 2 * kWsGroup;
+    for (int h = 0; h < 2 * seg; ++h) state_add_from<U>(st, w + (size_t)h * kWsGroup, lane);
+    state_publish<U>(st, smem, 0, g, c);  // buffer 0, read by the first chunk
+  }
 
   wait_copies_and_barrier();
-  for (int t = 0; t < p.n_chunks; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < p.n_chunks) {
+  for (int t = t_begin; t < t_end; ++t) {
+    const int cur = (t - t_begin) & 1;
+    if (t + 1 < t_end) {
       const uint32_t stage = hr.smem_lds + (cur ^ 1) * kStage;
       copy_one(hr.qr, hr.kr, hr.vr, 4 + 2 * U, (t + 1) * kChunk, N, stage, lane);
       copy_one(hr.qr, hr.kr, hr.vr, 5 + 2 * U, (t + 1) * kChunk, N, stage, lane);
     }
     const char* Ks = smem + cur * kStage + kQBytes;
     const char* Vs = Ks + kQBytes;
-
-    // ---- S += phi(K)^T V, KK += K^T K, ksum += sum k
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const char* k0 = Ks + (32 * m + 4 * g + (c >> 2)) * 32 + 8 * (c & 3);
-      const bf16x8 kc = __builtin_shufflevector(tr4(k0), tr4(k0 + 16 * 32), 0, 1, 2, 3, 4, 5, 6, 7);
-      float kf[8], kfs[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        kf[j] = (float)kc[j];  // k[token_j][c]
-        kfs[j] = kf[j] * kC2;
-      }
-      bf16x8 vfm[4];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) vfm[cb] = v_frag(Vs, m, cb, g, c);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        float f[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)  // k[token_j][4U + rb] from lane 4U + rb of this row
-          f[j] = __uint_as_float(row_bcast_feature<U>(__float_as_uint(kf[j]), rb)) * kfs[j];
-        const bf16x8 afeat = pack8(f);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          sq[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afeat, vfm[cb], sq[rb][cb], 0, 0, 0);
-      }
-      float fl[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) fl[j] = 0.5f * kf[j];
-      slin = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(fl), vfm[U], slin, 0, 0, 0);
-      bf16x8 ones;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ones[j] = (__bf16)(c == 0 ? 1.f : 0.f);
-      sconst = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, vfm[U], sconst, 0, 0, 0);
-      if (U == 0) {
-        kk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, kc, kk, 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ksum_part += kf[j];
-      }
-    }
-
-    // ---- publish the state after this chunk for the next one
-    char* Stn = smem + kOffSt + (cur ^ 1) * kStBytes;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        bf16x4 x;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = (__bf16)sq[rb][cb][i];
-        *reinterpret_cast<bf16x4*>(Stn + (16 * cb + c) * (kStRow * 2) + 2 * (16 * (4 * U + rb) + 4 * g)) = x;
-      }
-    {
-      bf16x4 xl, xc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xl[i] = (__bf16)slin[i];
-        xc[i] = (__bf16)sconst[i];
-      }
-      *reinterpret_cast<bf16x4*>(Stn + (16 * U + c) * (kStRow * 2) + 2 * (256 + 4 * g)) = xl;
-      *reinterpret_cast<bf16x4*>(Stn + (16 * U + c) * (kStRow * 2) + 2 * (272 + 4 * g)) = xc;
-    }
-    if (U == 0) {
-      __bf16* KKn = reinterpret_cast<__bf16*>(smem + kOffKK + (cur ^ 1) * kKKBytes);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const __bf16 hi = (__bf16)kk[i];
-        KKn[(4 * g + i) * kD + c] = hi;
-        KKn[256 + (4 * g + i) * kD + c] = (__bf16)(kk[i] - (float)hi);
-      }
-      const float ks = sum_across_halves(sum_across_16(ksum_part));
-      if (g == 0) reinterpret_cast<float*>(smem + kOffKs)[(cur ^ 1) * kD + c] = ks;
-    }
+    state_update<U>(st, Ks, Vs, g, c);
+    state_publish<U>(st, smem, cur ^ 1, g, c);  // the state after this chunk, for the next one
     wait_copies_and_barrier();
   }
 }
 
 // 8 waves: output waves 0-3 and state waves 4-7 (waves w and w + 4 share a SIMD, so every
-// SIMD runs one wave of each role). Both roles run n_chunks iterations with one barrier
-// each, after a common start: S^T buffer 0, KK buffer 0 and ksum buffer 0 are zeroed by all
-// waves before the first barrier.
+// SIMD runs one wave of each role); one workgroup per (batch, head, segment). Both roles
+// run the segment's chunks with one barrier each, after a common start: S^T buffer 0, KK
+// buffer 0 and ksum buffer 0 are zeroed by all waves, and after a barrier the state waves
+// of a later segment overwrite them with the state of the segments before it.
 __global__ __launch_bounds__(512) void based_fwd_kernel(const BasedParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[kLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const size_t bh = blockIdx.x / p.n_seg;
+  const int seg = (int)(blockIdx.x - bh * p.n_seg);
+  const int t_begin = seg * p.seg_chunks;
+  const int t_end = min(p.n_chunks, t_begin + p.seg_chunks);
   for (int i = tid; i < kStBytes / 4; i += 64 * kWaves) reinterpret_cast<uint32_t*>(smem + kOffSt)[i] = 0u;
   for (int i = tid; i < kKKBytes / 4; i += 64 * kWaves) reinterpret_cast<uint32_t*>(smem + kOffKK)[i] = 0u;
   if (tid < kD) reinterpret_cast<float*>(smem + kOffKs)[tid] = 0.f;
+  __syncthreads();
   switch (__builtin_amdgcn_readfirstlane(tid >> 6)) {
-    case 0: output_wave<0>(p, smem, lane); break;
-    case 1: output_wave<1>(p, smem, lane); break;
-    case 2: output_wave<2>(p, smem, lane); break;
-    case 3: output_wave<3>(p, smem, lane); break;
-    case 4: state_wave<0>(p, smem, lane); break;
-    case 5: state_wave<1>(p, smem, lane); break;
-    case 6: state_wave<2>(p, smem, lane); break;
-    default: state_wave<3>(p, smem, lane); break;
+    case 0: output_wave<0>(p, smem, lane, bh, t_begin, t_end); break;
+    case 1: output_wave<1>(p, smem, lane, bh, t_begin, t_end); break;
+    case 2: output_wave<2>(p, smem, lane, bh, t_begin, t_end); break;
+    case 3: output_wave<3>(p, smem, lane, bh, t_begin, t_end); break;
+    case 4: state_wave<0>(p, smem, lane, bh, seg, t_begin, t_end); break;
+    case 5: state_wave<1>(p, smem, lane, bh, seg, t_begin, t_end); break;
+    case 6: state_wave<2>(p, smem, lane, bh, seg, t_begin, t_end); break;
+    default: state_wave<3>(p, smem, lane, bh, seg, t_begin, t_end); break;
   }
+}
+
+// State pass of a split launch: one workgroup per (batch, head, segment but the last),
+// 8 waves in two groups of 4 state waves; group G takes the segment's chunks t_begin + 2i
+// + G, each from its own two LDS stages, and writes its sums to the workspace.
+template <int U>
+__device__ inline void state_pass_wave(const BasedParams& p, char* smem, int lane, int G, size_t bh,
+                                       int seg) {
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const int N = p.N;
+  const HeadRefs hr = head_refs(p, smem, bh);
+  const int t_begin = seg * p.seg_chunks;
+  const int n_pairs = (p.seg_chunks + 1) / 2;
+  auto load = [&](int i) {  // chunk t_begin + 2i + G into stage (2G + i % 2)
+    const int t = t_begin + 2 * i + G;
+    if (t >= t_begin + p.seg_chunks) return;
+    const uint32_t stage = hr.smem_lds + (2 * G + (i & 1)) * kStage;
+    if (U < 2) copy_one(hr.qr, hr.kr, hr.vr, 2 + U, t * kChunk, N, stage, lane);
+    copy_one(hr.qr, hr.kr, hr.vr, 4 + 2 * U, t * kChunk, N, stage, lane);
+    copy_one(hr.qr, hr.kr, hr.vr, 5 + 2 * U, t * kChunk, N, stage, lane);
+  };
+  StateRegs st;
+  state_zero(st);
+  load(0);
+  for (int i = 0; i < n_pairs; ++i) {
+    wait_copies_and_barrier();
+    if (i + 1 < n_pairs) load(i + 1);
+    // (the stage read here is refilled only after the next iteration's barrier)
+    if (t_begin + 2 * i + G < t_begin + p.seg_chunks) {
+      const char* Ks = smem + (2 * G + (i & 1)) * kStage + kQBytes;
+      state_update<U>(st, Ks, Ks + kQBytes, g, c);
+    }
+  }
+  float* w = p.ws + (bh * (size_t)(p.n_seg - 1) + seg) * 2 * kWsGroup + (size_t)G * kWsGroup;
+  state_store_to<U>(st, w, lane);
+}
+
+__global__ __launch_bounds__(512) void based_state_kernel(const BasedParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const size_t bh = blockIdx.x / (p.n_seg - 1);
+  const int seg = (int)(blockIdx.x - bh * (p.n_seg - 1));
+  switch (wave & 3) {
+    case 0: state_pass_wave<0>(p, smem, lane, wave >> 2, bh, seg); break;
+    case 1: state_pass_wave<1>(p, smem, lane, wave >> 2, bh, seg); break;
+    case 2: state_pass_wave<2>(p, smem, lane, wave >> 2, bh, seg); break;
+    default: state_pass_wave<3>(p, smem, lane, wave >> 2, bh, seg); break;
+  }
+}
+
+// Segments per head for a split launch: enough workgroups to cover the device's compute
+// units (queried once per device), but segments of at least kMinSegChunks chunks.
+constexpr int kMinSegChunks = 8;
+std::atomic<int> g_cus[64];
+int split_plan(int B, int H, int N, int* n_seg, int* seg_chunks) {
+  const int n_chunks = (N + kChunk - 1) / kChunk;
+  *n_seg = 1;
+  *seg_chunks = n_chunks;
+  if (B < 1 || H < 1 || N < 1) return BASED_EINVAL;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return BASED_ELAUNCH;
+  int cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      return BASED_ELAUNCH;
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  const int64_t heads = (int64_t)B * H;
+  if (heads >= cus) return BASED_OK;
+  const int want = (int)((cus + heads - 1) / heads);
+  const int cap = n_chunks / kMinSegChunks;
+  const int n = want < cap ? want : cap;
+  if (n < 2) return BASED_OK;
+  *seg_chunks = (n_chunks + n - 1) / n;
+  *n_seg = (n_chunks + *seg_chunks - 1) / *seg_chunks;
+  return BASED_OK;
 }
 
 }  // namespace
@@ -427,20 +595,48 @@ extern "C" {
 
 int based_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
               int dv, void* stream) {
+  return based_fwd_ws(q, k, v, o, nullptr, 0, B, H, N, d, dv, stream);
+}
+
+size_t based_fwd_workspace_bytes(int B, int H, int N) {
+  int n_seg = 0, seg_chunks = 0;
+  if (split_plan(B, H, N, &n_seg, &seg_chunks) != BASED_OK || n_seg < 2) return 0;
+  return (size_t)B * H * (n_seg - 1) * 2 * kWsGroup * sizeof(float);
+}
+
+int based_fwd_ws(const void* q, const void* k, const void* v, void* o, void* workspace,
+                 size_t workspace_bytes, int B, int H, int N, int d, int dv, void* stream) {
   if (!q || !k || !v || !o) return BASED_EINVAL;
   if (B < 1 || H < 1 || N < 1) return BASED_EINVAL;
   if (d != kD || dv != kDv) return BASED_EUNSUPPORTED;
-  if ((int64_t)N * kDv * 2 >= ((int64_t)1 << 31) || (int64_t)B * H >= ((int64_t)1 << 31)) return BASED_EINVAL;
+  if ((int64_t)N * kDv * 2 >= ((int64_t)1 << 31) || (int64_t)B * H >= ((int64_t)1 << 24)) return BASED_EINVAL;
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) != 0) return BASED_EALIGN;
+  if (workspace && ((uintptr_t)workspace & 255u) != 0) return BASED_EALIGN;
   BasedParams p;
   p.q = static_cast<const __bf16*>(q);
   p.k = static_cast<const __bf16*>(k);
   p.v = static_cast<const __bf16*>(v);
   p.o = static_cast<__bf16*>(o);
+  p.ws = nullptr;
   p.N = N;
   p.n_chunks = (N + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(based_fwd_kernel, dim3((unsigned)(B * H)), dim3(64 * kWaves), 0,
-                     static_cast<hipStream_t>(stream), p);
+  p.n_seg = 1;
+  p.seg_chunks = p.n_chunks;
+  if (workspace) {
+    int n_seg = 1, seg_chunks = p.n_chunks;
+    const int rc = split_plan(B, H, N, &n_seg, &seg_chunks);
+    if (rc != BASED_OK) return rc;
+    if (n_seg > 1 && workspace_bytes >= (size_t)B * H * (n_seg - 1) * 2 * kWsGroup * sizeof(float)) {
+      p.ws = static_cast<float*>(workspace);
+      p.n_seg = n_seg;
+      p.seg_chunks = seg_chunks;
+    }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.n_seg > 1)
+    hipLaunchKernelGGL(based_state_kernel, dim3((unsigned)((size_t)B * H * (p.n_seg - 1))), dim3(64 * kWaves),
+                       0, s, p);
+  hipLaunchKernelGGL(based_fwd_kernel, dim3((unsigned)((size_t)B * H * p.n_seg)), dim3(64 * kWaves), 0, s, p);
   if (hipGetLastError() != hipSuccess) return BASED_ELAUNCH;
   return BASED_OK;
 }

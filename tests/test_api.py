@@ -51,7 +51,7 @@ def test_header_declares_entry_points():
         ["gemm_bf16_nt", "gemm_strerror"]
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "based_fwd.h")).read(), flags=re.S)
     assert sorted(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(based_\w+)\s*\(", text, flags=re.M)) == \
-        ["based_fwd", "based_fwd_strerror"]
+        ["based_fwd", "based_fwd_strerror", "based_fwd_workspace_bytes", "based_fwd_ws"]
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "tile_calibrate.h")).read(), flags=re.S)
     assert sorted(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(tile_\w+)\s*\(", text, flags=re.M)) == \
         ["tile_mfma_calibrate", "tile_mfma_calibrate_out_floats"]
@@ -62,6 +62,7 @@ def test_exports_every_declared_symbol(lib):
     exported = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()],
                               capture_output=True, text=True, check=True).stdout.split()
     for name in declared_functions() + ["gemm_bf16_nt", "gemm_strerror", "based_fwd", "based_fwd_strerror",
+                                        "based_fwd_ws", "based_fwd_workspace_bytes",
                                         "tile_mfma_calibrate", "tile_mfma_calibrate_out_floats"]:
         assert hasattr(lib, name), f"{name} declared in include/ but not exported"
         assert name in exported
@@ -302,6 +303,15 @@ def test_based_codes_and_strerror(lib):
 ])
 def test_based_invalid_arguments_rejected(lib, args, code):
     assert lib.based_fwd(*args, None) == code
+
+
+def test_based_ws_checks_before_any_device_query(lib):
+    assert lib.based_fwd_ws(A, A, A, A, A + 16, 1 << 20, 1, 1, 64, 16, 64, None) == -3
+    assert lib.based_fwd_ws(None, A, A, A, None, 0, 1, 1, 64, 16, 64, None) == -1
+    assert lib.based_fwd_ws(A, A, A, A, None, 0, 1 << 12, 1 << 12, 64, 16, 64, None) == -1
+    assert lib.based_fwd_ws(A, A, A, A, None, 0, 1, 1, 64, 16, 32, None) == -2
+    assert lib.based_fwd_workspace_bytes(0, 1, 64) == 0
+    assert lib.based_fwd_workspace_bytes(1, 1, 0) == 0
 
 
 def test_based_binding_rejects_cpu_and_bad_shapes():

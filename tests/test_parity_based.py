@@ -120,6 +120,37 @@ def test_causality_and_determinism():
     assert torch.equal(o1, o3)
 
 
+# Split launches (B*H below the compute-unit count, at least 16 chunks of 64 tokens): each
+# head's sequence in segments of 8 or more chunks, a state pass over every segment but
+# the last, then one workgroup per segment. Ragged tails, odd and even chunk counts per
+# segment, and every element against the oracle; the unsplit launch on the same inputs
+# meets the same bar.
+SPLIT = [(1, 2, 2000), (2, 3, 1500), (1, 1, 4096), (3, 1, 1100)]
+
+
+@pytest.mark.parametrize("B,H,N", SPLIT, ids=[f"B{b}H{h}N{n}" for b, h, n in SPLIT])
+def test_split_launch_full_oracle(B, H, N):
+    from softmax_attention_fwd_amd.binding import based_fwd_workspace_bytes
+    assert based_fwd_workspace_bytes(B, H, N) > 0, "this shape should split"
+    w = BasedWorkload("split", B, H, N, seed=N + 7 * H)
+    q, k, v = based_inputs(w)
+    ref = oracle.based_linear_attention(f64(q), f64(k), f64(v))
+    check(run(q, k, v), ref, f"split B{B} H{H} N{N}")
+    check(run(q, k, v, split=False), ref, f"unsplit B{B} H{H} N{N}")
+
+
+def test_split_workspace_reused_and_dirty():
+    """A dirty, caller-given workspace gives the same bits as a fresh one."""
+    from softmax_attention_fwd_amd.binding import based_fwd_workspace_bytes
+    w = BasedWorkload("split-ws", 1, 2, 2000, seed=5)
+    q, k, v = (t.cuda() for t in based_inputs(w))
+    ws = torch.full((based_fwd_workspace_bytes(1, 2, 2000),), 255, dtype=torch.uint8, device="cuda")
+    o1 = based_fwd(q, k, v, workspace=ws)
+    o2 = based_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
 def test_writes_every_row_and_nothing_else():
     w = BasedWorkload("guard", 1, 1, 77, seed=73)
     q, k, v = (t.cuda() for t in based_inputs(w))
