@@ -517,13 +517,17 @@ void attn_bwd_dq_kernel(const BwdParams p) {
       // register r holds key kb0 + 8(r/4) + 4h + r%4 of query qrow
       const bool need_mask = (CAUSAL && kb0 + kBlk - 1 > q0) || (kb0 + kBlk > N);
       const int lim = (CAUSAL ? min(N, qrow + 1) : N) - kb0 - 4 * hi;  // key offset < lim
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(s[r] * p.c);
+      if (need_mask) {  // wave-uniform: only diagonal and ragged blocks pay for the selects
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) >= lim) pr[r] = 0.f;
+      }
       bf16x8 sb[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(s[r] * p.c);
-        if (need_mask && 8 * (r >> 2) + (r & 3) >= lim) pr = 0.f;
-        sb[r >> 3][r & 7] = (__bf16)(pr * dp[r]);
-      }
+      for (int r = 0; r < 16; ++r) sb[r >> 3][r & 7] = (__bf16)(pr[r] * dp[r]);
       // dQ^T += K^T dS^T over the block's 32 keys
 #pragma unroll
       for (int st = 0; st < 2; ++st)
