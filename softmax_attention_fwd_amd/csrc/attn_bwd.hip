@@ -395,16 +395,21 @@ void attn_bwd_dkdv1_kernel(const BwdParams p) {
       // offset 4h, against the limits
       const int lo_lim = CAUSAL ? key - qb0 - 4 * hi : -1;  // need query offset >= lo_lim
       const int hi_lim = N - qb0 - 4 * hi;                  // need query offset < hi_lim
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(s[r] * p.c);
+      if (need_mask) {  // wave-uniform: only diagonal and ragged blocks pay for the selects
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qo = 8 * (r >> 2) + (r & 3);
+          if (qo < lo_lim || qo >= hi_lim) pr[r] = 0.f;
+        }
+      }
       bf16x8 pb[2], sb[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(s[r] * p.c);
-        if (need_mask) {
-          const int qo = 8 * (r >> 2) + (r & 3);
-          if (qo < lo_lim || qo >= hi_lim) pr = 0.f;
-        }
-        if (kDv) pb[r >> 3][r & 7] = (__bf16)pr;
-        if (kDk) sb[r >> 3][r & 7] = (__bf16)(pr * dp[r]);
+        if (kDv) pb[r >> 3][r & 7] = (__bf16)pr[r];
+        if (kDk) sb[r >> 3][r & 7] = (__bf16)(pr[r] * dp[r]);
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 queries (two k-steps of 16)
 #pragma unroll
