@@ -18,7 +18,9 @@
 // quadratic features with first index a in [4u, 4u + 4) for all 64 value columns, plus the
 // linear and constant features for value columns [16u, 16u + 16). For chunk c the 4
 // output waves split the 64 tokens (16 each) and compute
-//   * O_inter^T = S^T phi(Q_c)^T from a bf16 copy of S^T in LDS (written after chunk c-1),
+//   * O_inter^T = S^T phi(Q_c)^T from a bf16 copy of S^T in LDS (written after chunk c-1;
+//     its linear rows carry the 1/2 of the query's linear features as well, which the
+//     query side then omits: both halves are powers of two, so the product is unchanged),
 //   * O_intra^T = V_c^T W^T with W the causal Taylor weights inside the chunk,
 //   * the normaliser: t0 + q . ksum / 4 + q^T KK q / 32 in fp32, with KK = sum k k^T and
 //     ksum = sum k over earlier chunks (KK enters an MFMA as a bf16 hi + lo pair),
@@ -226,7 +228,7 @@ __device__ inline void output_wave(const BasedParams& p, char* smem, int lane, s
         for (int j = 0; j < 8; ++j) f[j] = qa[ks] * (qb[j] * kC2);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) f[j] = g < 2 ? 0.5f * qb[j] : ((g == 2 && j == 0) ? 1.f : 0.f);
+        for (int j = 0; j < 8; ++j) f[j] = g < 2 ? qb[j] : ((g == 2 && j == 0) ? 1.f : 0.f);
       }
       const bf16x8 bfeat = pack8(f);
 #pragma unroll
@@ -308,7 +310,8 @@ __device__ inline void output_wave(const BasedParams& p, char* smem, int lane, s
 // and (wave 0) KK and this lane's share of ksum.
 struct StateRegs {
   f32x4 sq[4][4];  // quadratic features (a = 4U + rb, b = 4g + i) x value columns 16cb + c
-  f32x4 slin;      // linear features b = 4g + i (value / 2) x value columns 16U + c
+  f32x4 slin;      // sum of k[b] v, b = 4g + i, x value columns 16U + c (unscaled; S^T
+                   // gets a quarter: the 1/2 of the key and of the query feature)
   f32x4 sconst;    // row 0: sum of v over value columns 16U + c; rows 1-15 stay zero
   f32x4 kk;        // wave 0: KK[a = 4g + i][b = c]
   float ksum_part; // wave 0: sum of k[token][c] over this lane's tokens
@@ -353,10 +356,9 @@ __device__ inline void state_update(StateRegs& st, const char* Ks, const char* V
       for (int cb = 0; cb < 4; ++cb)
         st.sq[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afeat, vfm[cb], st.sq[rb][cb], 0, 0, 0);
     }
-    float fl[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) fl[j] = 0.5f * kf[j];
-    st.slin = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8(fl), vfm[U], st.slin, 0, 0, 0);
+    // linear features: the sums of k v, unscaled (their 1/2, and the query side's 1/2,
+    // are applied once when the state is published)
+    st.slin = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, vfm[U], st.slin, 0, 0, 0);
     bf16x8 ones;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ones[j] = (__bf16)(c == 0 ? 1.f : 0.f);
@@ -386,7 +388,7 @@ __device__ inline void state_publish(const StateRegs& st, char* smem, int buf, i
     bf16x4 xl, xc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      xl[i] = (__bf16)st.slin[i];
+      xl[i] = (__bf16)(0.25f * st.slin[i]);  // (k / 2) . (q / 2): both halves, exact
       xc[i] = (__bf16)st.sconst[i];
     }
     *reinterpret_cast<bf16x4*>(Stn + (16 * U + c) * (kStRow * 2) + 2 * (256 + 4 * g)) = xl;
