@@ -26,10 +26,11 @@
 //     ksum = sum k over earlier chunks (KK enters an MFMA as a bf16 hi + lo pair),
 //     plus the row sums of W,
 // while the state waves add phi(K_c)^T V_c to their part of S and publish the new bf16 S^T
-// for the next chunk. All products are v_mfma_f32_16x16x32_bf16. The quadratic features of K
-// are formed in registers: each lane holds k[token][b] for 8 tokens (transposing LDS
-// reads) and multiplies by k[token][a] taken from lane a of its 16-lane row (a DPP row
-// broadcast folded into the multiply).
+// for the next chunk. The products are v_mfma_f32_16x16x32_bf16, except those whose depth
+// is the 16 key features (in-chunk scores, KK q), which use v_mfma_f32_16x16x16_bf16.
+// The quadratic features of K are formed in registers: each lane holds k[token][b] for 8
+// tokens (transposing LDS reads) and multiplies by k[token][a] taken from lane a of its
+// 16-lane row (a DPP row broadcast folded into the multiply).
 // Chunk c+1's Q, K, V are copied global -> LDS (buffer_load ... lds) during chunk c;
 // rows past N read as zeros, so they add nothing to S, KK and ksum.
 #include <hip/hip_runtime.h>
@@ -119,6 +120,14 @@ __device__ inline uint32_t row_bcast_feature(uint32_t x, int rb) {
 __device__ inline float sum_across_16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// v_mfma_f32_16x16x16_bf16: the products whose depth is the 16 key features. Lane l holds
+// A row l % 16 and B column l % 16 at depth 4 (l / 16) .. + 3; C as in the 32-deep form.
+__device__ inline f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                   0, 0, 0);
 }
 
 // Transposing read of a 4-row x 16-column bf16 block: in every 16-lane row, lane c supplies
@@ -214,7 +223,8 @@ __device__ inline void output_wave(const BasedParams& p, char* smem, int lane, s
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) qb[j] = (float)qbv[j];
-    const bf16x8 bq_plain = g < 2 ? qbv : bf16x8{};  // q[tq][8g + j] for g < 2, else 0
+    // q[tq][4g .. 4g + 3]: the B operand of the 16-deep products over the 16 features
+    const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qs + tq * 32 + 8 * g);
 
     // ---- O_inter^T = S^T phi(Q)^T over the 288 (padded) features, 9 steps of 32
     f32x4 o[4];
@@ -244,8 +254,8 @@ __device__ inline void output_wave(const BasedParams& p, char* smem, int lane, s
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       if (kb <= W) {
-        const bf16x8 ak = g < 2 ? *reinterpret_cast<const bf16x8*>(Ks + (16 * kb + c) * 32 + 16 * g) : bf16x8{};
-        const f32x4 s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bq_plain, f32x4{}, 0, 0, 0);
+        const bf16x4 ak = *reinterpret_cast<const bf16x4*>(Ks + (16 * kb + c) * 32 + 8 * g);
+        const f32x4 s = mfma16(ak, q4, f32x4{});
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float x = 0.25f * s[i];
@@ -273,11 +283,10 @@ __device__ inline void output_wave(const BasedParams& p, char* smem, int lane, s
 
     // ---- normaliser: t0 + q . ksum / 4 + q^T KK q / 32 (earlier chunks) + row sum of W
     {
-      const bf16x8 khi = g < 2 ? *reinterpret_cast<const bf16x8*>(KKs + c * 32 + 16 * g) : bf16x8{};
-      const bf16x8 klo = g < 2 ? *reinterpret_cast<const bf16x8*>(KKs + 512 + c * 32 + 16 * g) : bf16x8{};
-      f32x4 u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, bq_plain, f32x4{}, 0, 0, 0);
-      u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(klo, bq_plain, u, 0, 0, 0);  // u[i] = (KK q)[4g + i]
-      const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(Qs + tq * 32 + 8 * g);
+      const bf16x4 khi = *reinterpret_cast<const bf16x4*>(KKs + c * 32 + 8 * g);
+      const bf16x4 klo = *reinterpret_cast<const bf16x4*>(KKs + 512 + c * 32 + 8 * g);
+      f32x4 u = mfma16(khi, q4, f32x4{});
+      u = mfma16(klo, q4, u);  // u[i] = (KK q)[4g + i]
       const f32x4 ks4 = *reinterpret_cast<const f32x4*>(kss + 4 * g);
       float zq = 0.f, zl = 0.f;
 #pragma unroll
