@@ -39,7 +39,11 @@ constexpr int kKeys = 32;                    // keys per wave tile
 constexpr int kChunkAlign = kWaves * kKeys;  // key chunks are multiples of this
 constexpr int kMaxQ = 32;
 constexpr float kRescaleLog2 = 8.0f;         // lazy-rescale threshold (log2 units)
-constexpr int kTargetWorkgroups = 1024;      // about four per compute unit
+// One workgroup per compute unit of the MI355X (256): the split kernel's 128 KiB of LDS
+// admits one workgroup per CU at a time, and a single round has no tail. Measured against
+// 1024 (four rounds): 7%, 39% and 1.4% faster on the three decode workloads (1 query x
+// 4096 keys x 256 heads, 8 x 16384 x 32, 1 x 131072 x 32).
+constexpr int kTargetWorkgroups = 256;
 
 struct DecParams {
   const __bf16* q;
