@@ -207,8 +207,13 @@ def test_decode_codes_and_strerror(lib):
 
 
 def test_decode_workspace_bytes(lib):
-    # 256 heads -> 4 key chunks each; partial O (fp32) and lse per chunk and query
-    assert lib.attn_decode_workspace_bytes(16, 16, 1, 4096, 128) == 4 * 256 * 128 * 4 + 4096
+    # about one workgroup per compute unit (256): 256 heads -> one key chunk each; partial
+    # O (fp32) and lse per chunk and query, each array rounded up to 256 bytes
+    assert lib.attn_decode_workspace_bytes(16, 16, 1, 4096, 128) == 1 * 256 * 128 * 4 + 1024
+    # 8 heads -> 32 chunks of 128 keys each
+    assert lib.attn_decode_workspace_bytes(1, 8, 1, 4096, 128) == 32 * 8 * 128 * 4 + 1024
+    # 4 heads of 200 keys -> at most ceil(200 / 128) = 2 chunks; 3 queries
+    assert lib.attn_decode_workspace_bytes(2, 2, 3, 200, 64) == 2 * 4 * 3 * 64 * 4 + 256
     assert lib.attn_decode_workspace_bytes(1, 1, 33, 100, 64) == 0   # Nq > 32
     assert lib.attn_decode_workspace_bytes(1, 1, 1, 100, 96) == 0    # unsupported D
     assert lib.attn_decode_workspace_bytes(0, 1, 1, 100, 64) == 0
