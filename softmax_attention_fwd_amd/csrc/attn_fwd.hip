@@ -502,10 +502,35 @@ void attn_fwd_pp_kernel(const Params p) {
   // workgroups than units (one per compute unit): workgroup b walks units b,
   // b + gridDim.x, ...; the XCD order is taken over the units, so each XCD runs
   // consecutive units of the same heads.
+  //
+  // With kPrefetchNext (non-causal, D = 128), a unit's Q rows and first K and V tiles are
+  // loaded while the workgroup's previous unit finishes (see copies), so only its first
+  // unit waits for them. At D = 64, where the kernel already uses 235 of its 256 registers,
+  // the extra live values spilled and the kernel measured 0-2% slower; D = 128 gained
+  // 0.5-1.5% at B16 H16 N4096.
+  constexpr bool kPrefetchNext = !CAUSAL && D == 128;
+  auto unit_index = [&](int gu) {
+    return CAUSAL ? remap_block(blockIdx.x, p.remap)
+                  : (p.remap ? (gu & 7) * (p.n_units >> 3) + (gu >> 3) : gu);
+  };
+  // the next unit's Q rows qrow + 32b, as the unit's own are loaded below
+  auto load_next_q = [&](bf16x8 (&dst)[QB][D / 16], const __bf16* Qh, int qrow) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      if (qrow + kQW * b < p.N) {
+        const bf16x8* src = reinterpret_cast<const bf16x8*>(Qh + (size_t)(qrow + kQW * b) * D) + hi;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) dst[b][s] = src[2 * s];
+      } else {
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) dst[b][s] = bf16x8{};
+      }
+    }
+  };
+  bf16x8 qf_carried[QB][D / 16];  // with kPrefetchNext, loaded by the previous unit
   for (int gu = blockIdx.x;; gu += gridDim.x) {
   if (!CAUSAL && gu >= p.n_units) break;
-  const int g = CAUSAL ? remap_block(blockIdx.x, p.remap)
-                       : (p.remap ? (gu & 7) * (p.n_units >> 3) + (gu >> 3) : gu);
+  const int g = unit_index(gu);
   const int bh = g / p.n_qtiles;
   int qt = g - bh * p.n_qtiles;
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;
@@ -567,18 +592,33 @@ void attn_fwd_pp_kernel(const Params p) {
   const uint32_t vbuf_lds[2] = {smem_lds + 2 * L::kTileBytes, smem_lds + 3 * L::kTileBytes};
   auto copy_k = [&](int t, int i0, int i1) { copy_range(krsrc, koff, LC::kPeriodK, t, kbuf_lds[t & 1], i0, i1); };
   auto copy_v = [&](int t, int i0, int i1) { copy_range(vrsrc, voff, LC::kPeriodV, t, vbuf_lds[t & 1], i0, i1); };
-  if (grp == 1) copy_k(0, 0, LC::kCopies);
-
-  bf16x8 qf[QB][D / 16];
+  // The workgroup's next unit: with kPrefetchNext its K(0), K(1) and Q rows are loaded in
+  // this unit's last slot pair, its V(0) after that pair's last barrier. Its offsets are
+  // formed where they are used, so that they hold no registers in the loop.
+  const bool has_next = kPrefetchNext && gu + (int)gridDim.x < p.n_units;
+  auto next_unit = [&](size_t& head_n, int& q0_n) {
+    const int g_n = unit_index(gu + (int)gridDim.x);
+    const int bh_n = g_n / p.n_qtiles;
+    head_n = (size_t)bh_n * (size_t)N * D;
+    q0_n = (g_n - bh_n * p.n_qtiles) * kBrW + wave * kQWave;
+  };
+  // A unit that the previous one did not prefetch (a workgroup's first unit, every unit
+  // where kPrefetchNext is off) loads its K(0) and Q rows here, and K(1) and V(0) in pair 0.
+  const bool prefetched = kPrefetchNext && gu != (int)blockIdx.x;
+  bf16x8 qf_unit[QB][D / 16];
+  bf16x8 (&qf)[QB][D / 16] = kPrefetchNext ? qf_carried : qf_unit;
+  if (!prefetched) {
+    if (grp == 1) copy_k(0, 0, LC::kCopies);
 #pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    if (qrow + kQW * b < N) {
-      const bf16x8* src = reinterpret_cast<const bf16x8*>(Qh + (size_t)(qrow + kQW * b) * D) + hi;
+    for (int b = 0; b < QB; ++b) {
+      if (qrow + kQW * b < N) {
+        const bf16x8* src = reinterpret_cast<const bf16x8*>(Qh + (size_t)(qrow + kQW * b) * D) + hi;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) qf[b][s] = src[2 * s];
-    } else {
+        for (int s = 0; s < D / 16; ++s) qf[b][s] = src[2 * s];
+      } else {
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) qf[b][s] = bf16x8{};
+        for (int s = 0; s < D / 16; ++s) qf[b][s] = bf16x8{};
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -722,16 +762,52 @@ void attn_fwd_pp_kernel(const Params p) {
   // issued by group 1 in the first slot of pair i (spread through its vector phase in the
   // steady state) and waited for at the end of the pair; K(i+1) goes to the K slot
   // that held K(i-1), last read in pair i-1, and V(i) to the V slot that held V(i-2), last
-  // read in pair i-1 too (two-slot rings). Group 0 runs, in pair i, the
-  // matrix phase of step i (P V of tile i-1, scores of tile i) and then the vector phase of
-  // tile i; group 1 runs the vector phase of tile i-1 and then the matrix phase of step i.
+  // read in pair i-1 too (two-slot rings). The last pair, ntiles, has none of this unit;
+  // with kPrefetchNext, both K slots and the Q registers being free there (last read in
+  // pair ntiles - 1), it issues the next unit's K(0), K(1) and Q (Q once the wave's last
+  // exponentials are done) and ends without waiting for them; the next unit's V(0) goes
+  // out after that pair's last barrier, so a prefetched unit has no copies in pair 0.
+  // Group 0 runs, in pair i, the matrix phase of step i (P V of tile i-1, scores of tile
+  // i) and then the vector phase of tile i; group 1 runs the vector phase of tile i-1 and
+  // then the matrix phase of step i.
   // Each group's sequence is straight-line code (first and last steps peeled), so the
   // accumulators keep their registers across the loop.
-  auto copies = [&](int i) {
+  auto copies_mid = [&](int i) {  // pairs 1 .. ntiles - 1, where every unit copies
     if (grp == 1) {
       if (i + 1 < ntiles) copy_k(i + 1, 0, LC::kCopies);
       if (i < ntiles) copy_v(i, 0, LC::kCopies);
     }
+  };
+  auto copies = [&](int i) {
+    if constexpr (!kPrefetchNext) {
+      copies_mid(i);
+    } else if (i == ntiles) {
+      if (has_next) {
+        if (grp == 1) {
+          size_t head_n;
+          int q0_n;
+          next_unit(head_n, q0_n);
+          const i32x4 krsrc_n = make_rsrc(p.k + head_n, head_bytes);
+          copy_range(krsrc_n, koff, LC::kPeriodK, 0, kbuf_lds[0], 0, LC::kCopies);
+          if (1 < ntiles) copy_range(krsrc_n, koff, LC::kPeriodK, 1, kbuf_lds[1], 0, LC::kCopies);
+        }
+      }
+    } else if (i > 0 || !prefetched) {
+      copies_mid(i);
+    }
+  };
+  // the next unit's Q rows, once this wave's last scores are consumed
+  auto prefetch_q = [&]() {
+    if (kPrefetchNext && has_next) {
+      size_t head_n;
+      int q0_n;
+      next_unit(head_n, q0_n);
+      load_next_q(qf, p.q + head_n, q0_n + col);
+    }
+  };
+  auto end_pair = [&](int i) {
+    if (kPrefetchNext && has_next && i == ntiles) __syncthreads();
+    else wait_copies_and_barrier();
   };
   // A full matrix phase: the P V MFMAs of tile i-1 (key step st, output block d, in that
   // order), then the score MFMAs of tile i (step st, key block j), each LDS read feeding
@@ -799,14 +875,14 @@ void attn_fwd_pp_kernel(const Params p) {
       }
       wait_copies_and_barrier();
       for (i = 1; i + 1 < T; ++i) {
-        copies(i);
+        copies_mid(i);
         matrix(i);
         __syncthreads();
         softmax(i, false, -1);
         wait_copies_and_barrier();
       }
       if (i < T) {  // i == T - 1 >= 1
-        copies(i);
+        copies_mid(i);
         matrix(i);
         __syncthreads();
         softmax(i, true, -1);
@@ -814,9 +890,10 @@ void attn_fwd_pp_kernel(const Params p) {
         ++i;
       }
       copies(i);  // i == T
+      prefetch_q();
       pv(T - 1);
       __syncthreads();
-      wait_copies_and_barrier();
+      end_pair(i);
       ++i;
     } else {
       copies(0);
@@ -833,7 +910,7 @@ void attn_fwd_pp_kernel(const Params p) {
         wait_copies_and_barrier();
       }
       for (; i < T; ++i) {
-        copies(i);
+        copies_mid(i);
         softmax(i - 1, false, -1);
         __syncthreads();
         matrix(i);
@@ -842,15 +919,24 @@ void attn_fwd_pp_kernel(const Params p) {
       copies(i);  // i == T
       softmax(T - 1, true, -1);
       __syncthreads();
+      prefetch_q();
       pv(T - 1);
-      wait_copies_and_barrier();
+      end_pair(i);
       ++i;
     }
   }
   for (; i <= ntiles; ++i) {
     copies(i);
+    if (kPrefetchNext && i == ntiles) prefetch_q();
     __syncthreads();
-    wait_copies_and_barrier();
+    end_pair(i);
+  }
+  // every read of this unit's V tiles is behind the last barrier
+  if (kPrefetchNext && has_next && grp == 1) {
+    size_t head_n;
+    int q0_n;
+    next_unit(head_n, q0_n);
+    copy_range(make_rsrc(p.v + head_n, head_bytes), voff, LC::kPeriodV, 0, vbuf_lds[0], 0, LC::kCopies);
   }
 
   if (wave_active) {

@@ -121,11 +121,15 @@ def test_kernels_bit_identical(B, H, N, D, causal):
 # Non-causal grids of more work units than compute units, ragged N (last key tile and last
 # query tile partial, down to one row), unit counts that are and are not multiples of 8
 # (XCD order on and off) and both head sizes: the ping-pong and four-wave kernels must agree
-# bit for bit, and sampled rows of the first and last head match the oracle.
+# bit for bit, and sampled rows of the first and last head match the oracle. At D = 128 a
+# workgroup loads its next unit's first tiles and Q rows during the current unit's last
+# pair, also after a unit whose last waves are idle (N = 4097, 300).
 LARGE_GRID_SHAPES = [
     # B, H, N, D
     (16, 20, 256, 128), (64, 16, 512, 128), (16, 16, 1024, 64), (5, 9, 2500, 64),
     (11, 7, 1000, 128), (4, 5, 4097, 128), (2, 130, 300, 128),
+    # a workgroup's next unit has a ragged K(0) (N < 64) or K(1) (64 < N < 128)
+    (4, 80, 50, 128), (3, 100, 100, 128),
     # D = 64 ping-pong waves hold two 32-query blocks: a last wave whose second block is
     # partly past N (545 = 512 + 33) and one whose second block is wholly past it (1600)
     (3, 5, 545, 64), (7, 3, 1600, 64),
