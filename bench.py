@@ -45,19 +45,19 @@ KERNEL_SOURCE = os.path.join(ROOT, "softmax_attention_fwd_amd", "csrc", "attn_fw
 
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (separate
 # runs), scaled by what the same counters read for a 512 MiB device-to-device copy: FETCH_SIZE
-# reported 262157.5 KiB for 524288 KiB read (x 2.0), WRITE_SIZE 524288 KiB for 524288 KiB
+# reported 262157.6 KiB for 524288 KiB read (x 2.0), WRITE_SIZE 524288 KiB for 524288 KiB
 # written (x 1.0). Valid only for the kernel source they were taken on; any other source
 # reports null.
 MEASURED_TRAFFIC = {
     "w3_b16h16n4096d128": {
-        "source_sha256": "31182ce5aed2311458c6e9c0182fa73ee0a738249fa9c0e3d4e6c2ea4b90e107",
-        "fetch_kib": 393409.8 * 2.0,
-        "write_kib": 266350.8 * 1.0,
+        "source_sha256": "af592611ad93359398693776b0f48f8e712b2fea4c837658e303b79919775fc6",
+        "fetch_kib": 393420.5 * 2.0,
+        "write_kib": 266841.5 * 1.0,
     },
     "w2_b16h16n1024d64": {
-        "source_sha256": "31182ce5aed2311458c6e9c0182fa73ee0a738249fa9c0e3d4e6c2ea4b90e107",
-        "fetch_kib": 49364.7 * 2.0,
-        "write_kib": 33793.9 * 1.0,
+        "source_sha256": "af592611ad93359398693776b0f48f8e712b2fea4c837658e303b79919775fc6",
+        "fetch_kib": 49364.5 * 2.0,
+        "write_kib": 33794.4 * 1.0,
     },
 }
 
