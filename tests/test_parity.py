@@ -130,6 +130,9 @@ LARGE_GRID_SHAPES = [
     (11, 7, 1000, 128), (4, 5, 4097, 128), (2, 130, 300, 128),
     # a workgroup's next unit has a ragged K(0) (N < 64) or K(1) (64 < N < 128)
     (4, 80, 50, 128), (3, 100, 100, 128),
+    # persistent D = 64 grids (more than 256 units of 512 queries) with ragged units: idle
+    # waves and partly filled query blocks
+    (4, 80, 50, 64), (3, 100, 545, 64), (2, 100, 1600, 64),
     # D = 64 ping-pong waves hold two 32-query blocks: a last wave whose second block is
     # partly past N (545 = 512 + 33) and one whose second block is wholly past it (1600)
     (3, 5, 545, 64), (7, 3, 1600, 64),
@@ -372,3 +375,8 @@ def test_workload_full_size_every_element(wid):
     print(f"[parity] {w.describe()} (all {w.B * w.H * w.N} rows): O max-abs {max_abs:.3e} "
           f"(worst head {worst}) rel-L2 {rel:.3e} lse max-abs {lse_err:.3e}", flush=True)
     assert max_abs <= O_MAX_ABS and rel <= O_REL_L2 and lse_err <= LSE_MAX_ABS
+    if wid == 5:
+        # Its peaked rows (scores drawn with sigma 2) leave this workload the least margin:
+        # 1.876e-2 against the 2e-2 bar with the kernel's present summation order, the same
+        # bits on every device. A change that moves it past 1.9e-2 stops here, before the bar.
+        assert max_abs <= 1.9e-2, f"workload 5 O max-abs {max_abs} is closing on the bar"
