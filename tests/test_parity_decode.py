@@ -66,6 +66,9 @@ SHAPES = [
     (2, 1, 16, 4096, 128, False, 1.0), (1, 2, 32, 2048, 64, True, 1.0),
     (1, 2, 32, 32, 128, True, 1.0), (1, 2, 7, 5000, 128, True, 2.0),
     (3, 1, 2, 300, 64, False, 2.0),
+    # more heads than compute units (little or no split), and one head whose ragged cache
+    # is split over the most workgroups
+    (16, 32, 1, 512, 128, True, 1.0), (1, 1, 1, 65537, 64, False, 1.0),
 ]
 
 
