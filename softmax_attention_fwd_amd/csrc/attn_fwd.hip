@@ -75,6 +75,8 @@ struct Params {
   int n_units;   // ping-pong kernel: B * H * n_qtiles work units (the grid may be smaller)
   int remap;     // 1: grid size (ping-pong: unit count) is a multiple of 8, use the XCD order
   float c;       // scale * log2(e)
+  int causal_pairs;  // causal ping-pong: 0, one unit per workgroup; else the number of (long,
+                     // short) unit pairs that a persistent grid walks
 };
 
 // Both halves of the wave receive max(x[lane], x[lane ^ 32]).
@@ -496,22 +498,35 @@ void attn_fwd_pp_kernel(const Params p) {
   const int col = lane & 31;
   const int hi = lane >> 5;
 
-  // Work units. Causal: one per workgroup (the loop below runs once), since the hardware
-  // dispatches the grid longest units first, which balances units of different lengths
-  // better than a fixed assignment. Non-causal: persistent when the launch has fewer
-  // workgroups than units (one per compute unit): workgroup b walks units b,
-  // b + gridDim.x, ...; the XCD order is taken over the units, so each XCD runs
-  // consecutive units of the same heads.
+  // Work units. Non-causal: persistent when the launch has fewer workgroups than units (one
+  // per compute unit): workgroup b walks units b, b + gridDim.x, ...; the XCD order is taken
+  // over the units, so each XCD runs consecutive units of the same heads. Causal: with
+  // causal_pairs = 0, one unit per workgroup (the loop below runs once), dispatched longest
+  // first; otherwise a persistent grid in which workgroup b, iteration it, takes the pair
+  // (b mod 8) * causal_pairs / 8 + b / 8 + (it / 2) * gridDim.x / 8 of its XCD's share: a
+  // head's query tiles n - 1 - j and j, the long unit first. Every pair holds the same number
+  // of key tiles, and an XCD's pairs cover consecutive heads.
   //
-  // With kPrefetchNext (non-causal, D = 128), a unit's Q rows and first K and V tiles are
-  // loaded while the workgroup's previous unit finishes (see copies), so only its first
-  // unit waits for them. At D = 64, where the kernel already uses 235 of its 256 registers,
-  // the extra live values spilled and the kernel measured 0-2% slower; D = 128 gained
-  // 0.5-1.5% at B16 H16 N4096.
-  constexpr bool kPrefetchNext = !CAUSAL && D == 128;
-  auto unit_index = [&](int gu) {
-    return CAUSAL ? remap_block(blockIdx.x, p.remap)
-                  : (p.remap ? (gu & 7) * (p.n_units >> 3) + (gu >> 3) : gu);
+  // With kPrefetchNext (D = 128), a unit's Q rows and first K and V tiles are loaded while
+  // the workgroup's previous unit finishes (see copies), so only its first unit waits for
+  // them. At D = 64, where the kernel already uses 235 of its 256 registers, the extra live
+  // values spilled and the kernel measured 0-2% slower; D = 128 gained 0.5-1.5% at B16 H16
+  // N4096.
+  constexpr bool kPrefetchNext = D == 128;
+  // the unit's index g: head g / n_qtiles, query tile g mod n_qtiles (causal: counted from
+  // the last tile)
+  auto unit_index = [&](int gu, int it) {
+    if constexpr (CAUSAL) {
+      if (p.causal_pairs == 0) return remap_block(blockIdx.x, p.remap);
+      const int half = p.n_qtiles >> 1;
+      const int pair = (int)(blockIdx.x & 7) * (p.causal_pairs >> 3) + (int)(blockIdx.x >> 3) +
+                       (it >> 1) * (int)(gridDim.x >> 3);
+      const int bh = pair / half;
+      const int j = pair - bh * half;
+      return bh * p.n_qtiles + ((it & 1) ? p.n_qtiles - 1 - j : j);
+    } else {
+      return p.remap ? (gu & 7) * (p.n_units >> 3) + (gu >> 3) : gu;
+    }
   };
   // the next unit's Q rows qrow + 32b, as the unit's own are loaded below
   auto load_next_q = [&](bf16x8 (&dst)[QB][D / 16], const __bf16* Qh, int qrow) {
@@ -528,9 +543,10 @@ void attn_fwd_pp_kernel(const Params p) {
     }
   };
   bf16x8 qf_carried[QB][D / 16];  // with kPrefetchNext, loaded by the previous unit
+  int it = 0;  // causal: this workgroup's unit count so far
   for (int gu = blockIdx.x;; gu += gridDim.x) {
   if (!CAUSAL && gu >= p.n_units) break;
-  const int g = unit_index(gu);
+  const int g = unit_index(gu, it);
   const int bh = g / p.n_qtiles;
   int qt = g - bh * p.n_qtiles;
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;
@@ -595,16 +611,23 @@ void attn_fwd_pp_kernel(const Params p) {
   // The workgroup's next unit: with kPrefetchNext its K(0), K(1) and Q rows are loaded in
   // this unit's last slot pair, its V(0) after that pair's last barrier. Its offsets are
   // formed where they are used, so that they hold no registers in the loop.
-  const bool has_next = kPrefetchNext && gu + (int)gridDim.x < p.n_units;
-  auto next_unit = [&](size_t& head_n, int& q0_n) {
-    const int g_n = unit_index(gu + (int)gridDim.x);
+  // more: this workgroup has a next unit (known here only where it is used)
+  bool more = false;
+  if constexpr (CAUSAL) more = p.causal_pairs > 0 && it + 1 < 2 * p.causal_pairs / (int)gridDim.x;
+  else if constexpr (kPrefetchNext) more = gu + (int)gridDim.x < p.n_units;
+  const bool has_next = kPrefetchNext && more;
+  auto next_unit = [&](size_t& head_n, int& q0_n, int& nt_n) {
+    const int g_n = unit_index(gu + (int)gridDim.x, it + 1);
     const int bh_n = g_n / p.n_qtiles;
+    int qt_n = g_n - bh_n * p.n_qtiles;
+    if (CAUSAL) qt_n = p.n_qtiles - 1 - qt_n;
     head_n = (size_t)bh_n * (size_t)N * D;
-    q0_n = (g_n - bh_n * p.n_qtiles) * kBrW + wave * kQWave;
+    q0_n = qt_n * kBrW + wave * kQWave;
+    nt_n = CAUSAL ? (min(N, (qt_n + 1) * kBrW) + kBc - 1) / kBc : ntiles;
   };
   // A unit that the previous one did not prefetch (a workgroup's first unit, every unit
   // where kPrefetchNext is off) loads its K(0) and Q rows here, and K(1) and V(0) in pair 0.
-  const bool prefetched = kPrefetchNext && gu != (int)blockIdx.x;
+  const bool prefetched = kPrefetchNext && (CAUSAL ? it > 0 : gu != (int)blockIdx.x);
   bf16x8 qf_unit[QB][D / 16];
   bf16x8 (&qf)[QB][D / 16] = kPrefetchNext ? qf_carried : qf_unit;
   if (!prefetched) {
@@ -785,11 +808,11 @@ void attn_fwd_pp_kernel(const Params p) {
       if (has_next) {
         if (grp == 1) {
           size_t head_n;
-          int q0_n;
-          next_unit(head_n, q0_n);
+          int q0_n, nt_n;
+          next_unit(head_n, q0_n, nt_n);
           const i32x4 krsrc_n = make_rsrc(p.k + head_n, head_bytes);
           copy_range(krsrc_n, koff, LC::kPeriodK, 0, kbuf_lds[0], 0, LC::kCopies);
-          if (1 < ntiles) copy_range(krsrc_n, koff, LC::kPeriodK, 1, kbuf_lds[1], 0, LC::kCopies);
+          if (1 < nt_n) copy_range(krsrc_n, koff, LC::kPeriodK, 1, kbuf_lds[1], 0, LC::kCopies);
         }
       }
     } else if (i > 0 || !prefetched) {
@@ -800,8 +823,8 @@ void attn_fwd_pp_kernel(const Params p) {
   auto prefetch_q = [&]() {
     if (kPrefetchNext && has_next) {
       size_t head_n;
-      int q0_n;
-      next_unit(head_n, q0_n);
+      int q0_n, nt_n;
+      next_unit(head_n, q0_n, nt_n);
       load_next_q(qf, p.q + head_n, q0_n + col);
     }
   };
@@ -934,8 +957,8 @@ void attn_fwd_pp_kernel(const Params p) {
   // every read of this unit's V tiles is behind the last barrier
   if (kPrefetchNext && has_next && grp == 1) {
     size_t head_n;
-    int q0_n;
-    next_unit(head_n, q0_n);
+    int q0_n, nt_n;
+    next_unit(head_n, q0_n, nt_n);
     copy_range(make_rsrc(p.v + head_n, head_bytes), voff, LC::kPeriodV, 0, vbuf_lds[0], 0, LC::kCopies);
   }
 
@@ -960,7 +983,10 @@ void attn_fwd_pp_kernel(const Params p) {
       }
     }
   }
-  if (CAUSAL) break;
+  if constexpr (CAUSAL) {
+    if (!more) break;
+    ++it;
+  }
   }  // work units
 }
 
@@ -1038,6 +1064,8 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
   p.N = N;
   p.n_qtiles = (int)n_qtiles;
   p.remap = (grid % 8 == 0) ? 1 : 0;
+  p.n_units = 0;
+  p.causal_pairs = 0;
   p.c = scale * kLog2e;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1057,16 +1085,23 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse
     p.n_qtiles = (int)n_qtiles_pp;
     p.n_units = (int)grid_pp;
     p.remap = (grid_pp % 8 == 0) ? 1 : 0;
-    // non-causal launches with more units than compute units: a persistent grid of one
-    // workgroup per compute unit (a multiple of 8: the same share of every XCD)
+    // Launches with more units than compute units: a persistent grid of one workgroup per
+    // compute unit (a multiple of 8: the same share of every XCD). Causal D = 128 launches
+    // take it when a head's query tiles pair up (an even count) and the pairs split evenly
+    // over the grid; otherwise one unit per workgroup, longest first.
     int cus = 0;
-    if (!causal) {
+    if (!causal || D == 128) {
       const int rc = device_cus(&cus);
       if (rc != ATTN_FWD_OK) return rc;
     }
-    const int64_t persistent = (!causal && cus >= 8) ? cus / 8 * 8 : 0;
-    const dim3 gpp((unsigned)(persistent > 0 && grid_pp > persistent ? persistent : grid_pp)),
-        bpp(64 * kWavesPP);
+    const int64_t per_cu = cus >= 8 ? cus / 8 * 8 : 0;
+    int64_t persistent = (!causal && per_cu > 0 && grid_pp > per_cu) ? per_cu : 0;
+    if (causal && D == 128 && per_cu > 0 && grid_pp > per_cu && n_qtiles_pp % 2 == 0 &&
+        (grid_pp / 2) % per_cu == 0) {
+      persistent = per_cu;
+      p.causal_pairs = (int)(grid_pp / 2);
+    }
+    const dim3 gpp((unsigned)(persistent > 0 ? persistent : grid_pp)), bpp(64 * kWavesPP);
     if (D == 64) {
       if (causal) hipLaunchKernelGGL((attn_fwd_pp_kernel<64, 64, true>), gpp, bpp, 0, s, p);
       else hipLaunchKernelGGL((attn_fwd_pp_kernel<64, 64, false>), gpp, bpp, 0, s, p);
