@@ -43,7 +43,11 @@ def job(seed: int):
     c = gemm_nt(a, b)
     bq, bk, bv = randn(g, 1, 2, 2000 + seed, 16), randn(g, 1, 2, 2000 + seed, 16), randn(g, 1, 2, 2000 + seed, 64)
     ob = based_fwd(bq, bk, bv)  # 2 heads: the split launch with a workspace
-    return [o, lse, dq, dk, dv, od, ld, c, ob]
+    # the persistent forward grids: 512 (long, short) causal query-tile pairs, or 512 units
+    Hp = 32 if causal else 16
+    qp, kp, vp = (randn(g, 4, Hp, 2048, 128) for _ in range(3))
+    op, lp = attn_fwd(qp, kp, vp, causal=causal)
+    return [o, lse, dq, dk, dv, od, ld, c, ob, op, lp]
 
 
 def test_two_threads_on_two_streams_match_serial():
@@ -71,7 +75,8 @@ def test_two_threads_on_two_streams_match_serial():
     assert not errors, f"worker raised: {errors[0]!r}"
     serial = {s: job(s) for s in seeds}
     torch.cuda.synchronize()
-    names = ["o", "lse", "dq", "dk", "dv", "decode o", "decode lse", "gemm c", "based o"]
+    names = ["o", "lse", "dq", "dk", "dv", "decode o", "decode lse", "gemm c", "based o",
+             "persistent o", "persistent lse"]
     for s in seeds:
         for name, x, y in zip(names, serial[s], results[s]):
             assert torch.equal(x, y), f"seed {s}: {name} differs from the serial result"
