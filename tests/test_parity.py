@@ -409,3 +409,47 @@ def test_workload_full_size_every_element(wid):
         # 1.876e-2 against the 2e-2 bar with the kernel's present summation order, the same
         # bits on every device. A change that moves it past 1.9e-2 stops here, before the bar.
         assert max_abs <= 1.9e-2, f"workload 5 O max-abs {max_abs} is closing on the bar"
+
+
+# ------------------------------------------------------------ sequences of a million keys
+LONG = [
+    # B, H, N, D, causal: one head of 2^20 keys (causal: the persistent grid of query-tile
+    # pairs), a ragged 2^20 - 37 at D = 64 (persistent, two query blocks per wave), and two
+    # heads of 2^19 at causal D = 64 (the four-wave kernel)
+    (1, 1, 1 << 20, 128, False),
+    (1, 1, 1 << 20, 128, True),
+    (1, 1, (1 << 20) - 37, 64, False),
+    (1, 2, 1 << 19, 64, True),
+]
+
+
+@pytest.mark.parametrize("B,H,N,D,causal", LONG,
+                         ids=[f"B{b}H{h}N{n}D{d}{'c' if c else 'n'}" for b, h, n, d, c in LONG])
+def test_long_sequence_sampled(B, H, N, D, causal):
+    """Sampled rows of sequences far longer than any workload: the fp32 running sum l then
+    adds up 2^14 key tiles, and the byte offsets of K, V and O span up to 256 MiB a head."""
+    print(f"[parity] long sequence B{B} H{H} N{N} D{D} causal={causal}", flush=True)
+    q, k, v = make_qkv(B, H, N, D, seed=4242 + N % 97 + D)
+    o, lse = run(q, k, v, causal)
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    rng = np.random.default_rng(N + D)
+    fixed = [0, 1, 31, 32, 63, 64, 255, 256, 511, 512, N // 2, N - 513, N - 257, N - 256,
+             N - 65, N - 64, N - 33, N - 32, N - 2, N - 1]
+    rows = []
+    for b in range(B):
+        for h in range(H):
+            picks = sorted({i for i in fixed if 0 <= i < N} | set(int(x) for x in rng.integers(0, N, 6)))
+            rows += [(b, h, i) for i in picks]
+    o_ref = np.empty((len(rows), D))
+    lse_ref = np.empty(len(rows))
+    for b in range(B):
+        for h in range(H):
+            items = [(r, i) for r, (bb, hh, i) in enumerate(rows) if (bb, hh) == (b, h)]
+            qh, kh, vh = (f64(t[b:b + 1, h:h + 1]) for t in (q, k, v))
+            ro, rl = oracle.attention_rows(qh, kh, vh, [(0, 0, i) for _, i in items], causal)
+            for (r, _), oo, ll in zip(items, ro, rl):
+                o_ref[r], lse_ref[r] = oo, ll
+            del qh, kh, vh
+    idx = [torch.tensor([x[j] for x in rows]) for j in range(3)]
+    check(o.cpu()[idx[0], idx[1], idx[2]], lse.cpu()[idx[0], idx[1], idx[2]], o_ref, lse_ref,
+          f"B{B} H{H} N{N} D{D} {'causal' if causal else 'non-causal'} ({len(rows)} sampled rows)")
